@@ -1,0 +1,462 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each pin is a small check function; the tests run it on the oracle as written
+and, for the pins that guard arithmetic, on a copy of the oracle with a
+planted mistake (a dropped term, a wrong sign, a swapped bit order...), which
+the pin must catch.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import accounting, encode, gemv, pack
+from synth import WORKLOADS, make_weights, make_x, outlier_count
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16bits(a):
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Pin 1: the CSR worked example printed on the SpQR page
+# ---------------------------------------------------------------------------
+def _spqr_example_matrix(seed=0):
+    g = _golden("spqr_csr_example.json")
+    M, K = g["shape"]
+    rng = np.random.default_rng(seed)
+    W = rng.uniform(-g["bulk_abs_max"], g["bulk_abs_max"], size=(M, K))
+    for i, j, v in g["outliers"]:
+        W[i, j] = v
+    return W.astype(np.float16), g
+
+
+def check_csr_example(bits, fmt, seed=0):
+    W, g = _spqr_example_matrix(seed)
+    x = np.ones(W.shape[1])
+    enc = encode.encode(W, bits, fmt, len(g["outliers"]), 16, sens=x)
+    ok = (list(enc["col_idx"]) == g["col_idx"]
+          and list(enc["row_ptr"]) == g["row_ptr"]
+          and [hex(v) for v in _f16bits(enc["values"])] == g["values_fp16_bits"]
+          and list(enc["values"].astype(np.float64)) == g["values_decimal"])
+    D = gemv.decode(enc)
+    holes_zero = all(D[i, j] == 0.0 for i, j, _ in g["outliers"])
+    return ok and holes_zero
+
+
+@pytest.mark.parametrize("bits,fmt", [(3, "uniform"), (4, "uniform"), (3, "lut"), (4, "lut")])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_csr_worked_example(bits, fmt, seed):
+    assert check_csr_example(bits, fmt, seed)
+
+
+def test_csr_worked_example_catches_sign_flip(monkeypatch):
+    orig = encode.build_csr
+
+    def flipped(W16, hole, D):
+        rp, ci, v = orig(W16, hole, D)
+        return rp, ci, (-v.astype(np.float64)).astype(np.float16)
+    monkeypatch.setattr(encode, "build_csr", flipped)
+    assert not check_csr_example(3, "uniform")
+
+
+def test_csr_worked_example_catches_column_major_order(monkeypatch):
+    orig = encode.build_csr
+
+    def colmajor(W16, hole, D):
+        rp, ci, v = orig(W16, hole, D)
+        c, r = np.nonzero(hole.T)          # column-major traversal
+        return rp, c.astype(np.int32), v
+    monkeypatch.setattr(encode, "build_csr", colmajor)
+    assert not check_csr_example(3, "uniform")
+
+
+# ---------------------------------------------------------------------------
+# Pin 2: W_dense + W_sparse reproduces every outlier exactly
+# ---------------------------------------------------------------------------
+SMALL = {
+    "tiny_u4": (None, None),
+    "attn7b_u3": (48, 4096),
+    "mlp7b_lut3": (24, 4096),
+    "mlp70b_lut4": (16, 8192),
+    "block7b_u3": (64, 2048),
+}
+
+
+def _small_encoding(name):
+    wl = WORKLOADS[name]
+    M, K = SMALL[name]
+    W, planted = make_weights(wl, 0, M, K)
+    M, K = W.shape
+    x = make_x(wl, max(wl.batches), K, 0, M)
+    enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M, K), wl.group or 16,
+                        sens=x[0].astype(np.float64) ** 2)
+    return wl, W, planted, x, enc
+
+
+_CACHE = {}
+
+
+def small(name):
+    if name not in _CACHE:
+        _CACHE[name] = _small_encoding(name)
+    return _CACHE[name]
+
+
+def check_exact_outliers(W, enc):
+    D = gemv.decode(enc)
+    r, c = np.nonzero(enc["mask"])
+    recon = D[r, c] + enc["values"].astype(np.float64)
+    return bool(np.array_equal(recon, W.astype(np.float64)[r, c]))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dense_plus_sparse_exact_at_outliers(name):
+    wl, W, planted, x, enc = small(name)
+    assert np.array_equal(enc["mask"], planted)
+    assert check_exact_outliers(W, enc)
+    assert enc["row_ptr"][-1] == planted.sum()
+
+
+def test_exactness_catches_nonzero_hole(monkeypatch):
+    wl, W, planted, x, enc = small("tiny_u4")
+    orig = encode.quant_uniform
+
+    def bad(W16, hole, bits, group):
+        q, s, z = orig(W16, hole, bits, group)
+        q = q.copy()
+        q[hole] = np.minimum(q[hole] + 1, (1 << bits) - 1)
+        return q, s, z
+    monkeypatch.setattr(encode, "quant_uniform", bad)
+    enc2 = encode.encode(W, 4, "uniform", outlier_count(wl, *W.shape), 16)
+    assert not check_exact_outliers(W, enc2)
+
+
+# ---------------------------------------------------------------------------
+# Pin 3: brute-force GEMV straight from the packed bytes (pure Python loops)
+# ---------------------------------------------------------------------------
+def brute_force_y(enc, X16):
+    """Triple loop over the canonical arrays; bits extracted one by one."""
+    M, K, b = enc["M"], enc["K"], enc["bits"]
+    packed = np.asarray(enc["codes_packed"])
+    rp, ci, va = enc["row_ptr"], enc["col_idx"], enc["values"]
+    Y = []
+    for xrow in np.asarray(X16):
+        x = [float(v) for v in xrow]
+        y = []
+        for i in range(M):
+            row = [int(v) for v in packed[i]]
+            acc = 0.0
+            for j in range(K):
+                q = 0
+                for t in range(b):
+                    p = j * b + t
+                    q |= ((row[p // 8] >> (p % 8)) & 1) << t
+                if enc["fmt"] == "uniform":
+                    g = j // enc["group"]
+                    d = float(enc["scales"][i, g]) * (q - float(enc["zeros"][i, g]))
+                else:
+                    d = float(enc["lut"][i, q])
+                acc += d * x[j]
+            for p in range(int(rp[i]), int(rp[i + 1])):
+                acc += float(va[p]) * x[int(ci[p])]
+            y.append(acc)
+        Y.append(y)
+    return np.array(Y)
+
+
+def _tiny_enc(bits, fmt, n_out, seed, M=6, K=64, B=2):
+    rng = np.random.default_rng(seed)
+    W = (0.02 * rng.standard_normal((M, K))).astype(np.float16)
+    idx = rng.choice(M * K, size=n_out, replace=False)
+    W.ravel()[idx] = rng.uniform(0.3, 2.0, size=n_out) * np.where(rng.integers(0, 2, n_out) > 0, 1, -1)
+    x = rng.standard_normal((B, K)).astype(np.float16)
+    enc = encode.encode(W, bits, fmt, n_out, 16, sens=x[0].astype(np.float64) ** 2)
+    return W, x, enc
+
+
+def check_brute_force(enc, x):
+    y, A = gemv.gemv(enc, x)
+    yb = brute_force_y(enc, x)
+    return bool(np.all(np.abs(y - yb) <= 1e-12 * (A + 1.0)))
+
+
+@pytest.mark.parametrize("bits,fmt", [(3, "uniform"), (4, "uniform"), (3, "lut"), (4, "lut")])
+@pytest.mark.parametrize("n_out", [0, 5])
+def test_gemv_matches_brute_force(bits, fmt, n_out):
+    W, x, enc = _tiny_enc(bits, fmt, n_out, seed=bits * 10 + n_out)
+    assert check_brute_force(enc, x)
+
+
+def test_brute_force_catches_dropped_sparse_term(monkeypatch):
+    W, x, enc = _tiny_enc(3, "uniform", 5, seed=7)
+    monkeypatch.setattr(gemv, "sparse_rows",
+                        lambda e, rows: (np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros(0)))
+    assert not check_brute_force(enc, x)
+
+
+def test_brute_force_catches_zero_sign(monkeypatch):
+    W, x, enc = _tiny_enc(4, "uniform", 5, seed=8)
+    orig = gemv.decode_rows
+
+    def plus_z(e, rows=None, codes=None):
+        e2 = dict(e)
+        e2["zeros"] = (-e["zeros"].astype(np.float64)).astype(np.float16)
+        return orig(e2, rows, codes)
+    monkeypatch.setattr(gemv, "decode_rows", plus_z)
+    assert not check_brute_force(enc, x)
+
+
+def test_brute_force_catches_transposed_lut(monkeypatch):
+    W, x, enc = _tiny_enc(3, "lut", 5, seed=9)
+    orig = gemv.decode_rows
+
+    def reversed_lut(e, rows=None, codes=None):
+        e2 = dict(e)
+        e2["lut"] = e["lut"][:, ::-1].copy()
+        return orig(e2, rows, codes)
+    monkeypatch.setattr(gemv, "decode_rows", reversed_lut)
+    assert not check_brute_force(enc, x)
+
+
+def test_zero_outlier_case_is_plain_dequant_gemv():
+    """With no outliers the CSR is empty and y = D x exactly as a dense product."""
+    for bits, fmt in [(3, "uniform"), (4, "lut")]:
+        W, x, enc = _tiny_enc(bits, fmt, 0, seed=11)
+        assert enc["row_ptr"].tolist() == [0] * (enc["M"] + 1)
+        assert len(enc["col_idx"]) == 0 and len(enc["values"]) == 0
+        D = gemv.decode(enc)
+        y, _ = gemv.gemv(enc, x)
+        assert np.array_equal(y, x.astype(np.float64) @ D.T)
+
+
+def test_sparse_scatter_equals_dense_product():
+    """y = (D + scatter(CSR)) x, using a dense fp64 product of the summed matrix."""
+    for name in ["tiny_u4", "mlp7b_lut3"]:
+        wl, W, planted, x, enc = small(name)
+        D = gemv.decode(enc)
+        S = gemv.sparse_dense(enc)
+        y, A = gemv.gemv(enc, x)
+        y2 = x.astype(np.float64) @ (D + S).T
+        assert np.all(np.abs(y - y2) <= 1e-12 * (A + 1.0))
+        # and dense + sparse equals W wherever it is an outlier, decoded dense elsewhere
+        assert np.array_equal((D + S)[planted], W.astype(np.float64)[planted])
+
+
+# ---------------------------------------------------------------------------
+# Pin 4: canonical bitstream
+# ---------------------------------------------------------------------------
+def check_bitstream_golden():
+    g = _golden("bitstream_lsb_first.json")
+    for case in g["cases"]:
+        codes = np.array([case["codes"]], dtype=np.uint8)
+        got = pack.pack_bitstream(codes, case["bits"])[0]
+        if [int(v) for v in got] != [int(c, 16) for c in case["bytes"]]:
+            return False
+        if not np.array_equal(pack.unpack_bitstream(got[None, :], case["bits"], codes.shape[1]), codes):
+            return False
+    return True
+
+
+def test_bitstream_golden():
+    assert check_bitstream_golden()
+
+
+def test_bitstream_golden_catches_msb_first(monkeypatch):
+    def msb_first(codes, bits):
+        M, K = codes.shape
+        planes = (codes[:, :, None].astype(np.uint16) >> np.arange(bits)[::-1]) & 1
+        return np.packbits(planes.reshape(M, K * bits).astype(np.uint8), axis=1, bitorder="big")
+    monkeypatch.setattr(pack, "pack_bitstream", msb_first)
+    assert not check_bitstream_golden()
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_bitstream_roundtrip_every_value_every_offset(bits):
+    K = 32 * (1 << bits)
+    # every code value appears at every position of a 32-code (whole-dword) period
+    codes = np.array([[(j + r) % (1 << bits) for j in range(K)] for r in range(1 << bits)], dtype=np.uint8)
+    packed = pack.pack_bitstream(codes, bits)
+    assert packed.shape == (1 << bits, K * bits // 8)
+    assert np.array_equal(pack.unpack_bitstream(packed, bits, K), codes)
+
+
+def test_bitstream_row_stride():
+    codes = np.random.default_rng(3).integers(0, 8, size=(5, 64)).astype(np.uint8)
+    packed = pack.pack_bitstream(codes, 3)
+    for i in range(5):
+        assert np.array_equal(packed[i], pack.pack_bitstream(codes[i:i + 1], 3)[0])
+
+
+# ---------------------------------------------------------------------------
+# Pin 5: uniform group quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_u4", "attn7b_u3", "block7b_u3"])
+def test_uniform_codes_are_nearest_grid_points(name):
+    wl, W, planted, x, enc = small(name)
+    L = (1 << wl.bits) - 1
+    w = W.astype(np.float64)
+    s = np.repeat(enc["scales"].astype(np.float64), wl.group, axis=1)
+    z = np.repeat(enc["zeros"].astype(np.float64), wl.group, axis=1)
+    grid = s[..., None] * (np.arange(L + 1)[None, None, :] - z[..., None])   # [M, K, L+1]
+    best = np.min(np.abs(w[..., None] - grid), axis=2)
+    D = gemv.decode(enc)
+    inl = ~planted
+    # the chosen code is a nearest grid point (rint ties may pick either neighbour)
+    assert np.all(np.abs(w - D)[inl] <= best[inl] + 1e-15)
+    assert np.all(enc["codes"] <= L)
+    # zero points are exact integers in [0, L]
+    zz = enc["zeros"].astype(np.float64)
+    assert np.array_equal(zz, np.rint(zz)) and zz.min() >= 0 and zz.max() <= L
+
+
+@pytest.mark.parametrize("name", ["tiny_u4", "attn7b_u3"])
+def test_uniform_error_bound(name):
+    """|w - d| <= scale/2 + L*|scale - (hi - lo)/L| for every non-outlier."""
+    wl, W, planted, x, enc = small(name)
+    L = (1 << wl.bits) - 1
+    g = wl.group
+    w = W.astype(np.float64).reshape(W.shape[0], -1, g)
+    h = planted.reshape(w.shape)
+    lo = np.minimum(0, np.where(h, np.inf, w).min(axis=2))
+    hi = np.maximum(0, np.where(h, -np.inf, w).max(axis=2))
+    s = enc["scales"].astype(np.float64)
+    bound = s / 2 + L * np.abs(s - (hi - lo) / L)
+    err = np.abs(w - gemv.decode(enc).reshape(w.shape))
+    assert np.all(np.where(h, 0, err) <= bound[..., None] + 1e-15)
+
+
+def test_uniform_exact_on_grid():
+    """Weights that already lie on a representable grid decode exactly."""
+    rng = np.random.default_rng(5)
+    scale = 2.0 ** -7
+    q = rng.integers(0, 16, size=(4, 64))
+    z = 5
+    q[:, ::16] = 0      # make every group span the full code range
+    q[:, 1::16] = 15
+    W = (scale * (q - z)).astype(np.float16)
+    enc = encode.encode(W, 4, "uniform", 0, 16)
+    assert np.array_equal(gemv.decode(enc), W.astype(np.float64))
+    assert np.all(enc["scales"].astype(np.float64) == scale)
+    assert np.all(enc["zeros"].astype(np.float64) == z)
+
+
+# ---------------------------------------------------------------------------
+# Pin 6: weighted Lloyd-Max
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_lloyd_objective_never_increases(seed):
+    rng = np.random.default_rng(seed)
+    w = 0.02 * rng.standard_normal(500)
+    s = rng.standard_normal(500) ** 2
+    hist = []
+    cent, zi = encode.lloyd_row(w, s, 8, history=hist)
+    assert all(b <= a + 1e-15 for a, b in zip(hist, hist[1:]))
+    assert cent[zi] == 0.0 and np.all(np.diff(cent) >= 0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lloyd_terminates_at_fixed_point(seed):
+    rng = np.random.default_rng(100 + seed)
+    w = 0.02 * rng.standard_normal(300)
+    s = rng.uniform(0.1, 3.0, 300)
+    cent, zi = encode.lloyd_row(w, s, 16)
+    a = encode.nearest(w, cent)
+    for c in range(16):
+        if c == zi or not np.any(a == c):
+            continue
+        mean = np.sum(s[a == c] * w[a == c]) / np.sum(s[a == c])
+        assert abs(mean - cent[c]) <= 1e-15 * max(1.0, abs(mean)) + 1e-18
+
+
+def _brute_force_pinned_optimum(w, s, C):
+    """Global optimum over every assignment of points to C clusters, one pinned at 0."""
+    import itertools
+    best = np.inf
+    n = len(w)
+    for assign in itertools.product(range(C), repeat=n):
+        a = np.array(assign)
+        sse = 0.0
+        for c in range(C):
+            sel = a == c
+            if not sel.any():
+                continue
+            if c == 0:
+                sse += np.sum(s[sel] * w[sel] ** 2)
+            else:
+                m = np.sum(s[sel] * w[sel]) / np.sum(s[sel])
+                sse += np.sum(s[sel] * (w[sel] - m) ** 2)
+        best = min(best, sse)
+    return best
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_lloyd_not_below_global_optimum(seed):
+    rng = np.random.default_rng(200 + seed)
+    w = rng.standard_normal(7)
+    s = rng.uniform(0.2, 2.0, 7)
+    cent, zi = encode.lloyd_row(w, s, 3)
+    a = encode.nearest(w, cent)
+    sse = encode.weighted_sse(w, s, cent, a)
+    opt = _brute_force_pinned_optimum(w, s, 3)
+    assert sse >= opt - 1e-12
+
+
+def test_lloyd_recovers_exact_clusters():
+    """Data made of C-1 distinct values with equal mass are reproduced exactly."""
+    vals = np.array([-0.75, -0.5, -0.25, 0.125, 0.25, 0.5, 1.0])
+    w = np.repeat(vals, 8)
+    s = np.ones_like(w)
+    cent, zi = encode.lloyd_row(w, s, 8)
+    assert sorted(set(cent.tolist()) - {0.0}) == sorted(vals.tolist())
+    W = np.tile(w, (2, 1)).astype(np.float16)
+    enc = encode.encode(W, 3, "lut", 0, sens=np.ones(W.shape[1]))
+    assert np.array_equal(gemv.decode(enc), W.astype(np.float64))
+
+
+def test_lut_codes_nearest_and_zero_pinned():
+    wl, W, planted, x, enc = small("mlp7b_lut3")
+    lut = enc["lut"].astype(np.float64)
+    assert np.all(np.diff(lut, axis=1) >= 0)
+    assert np.all(np.any(lut == 0.0, axis=1))
+    w = W.astype(np.float64)
+    dist = np.abs(w[:, :, None] - lut[:, None, :])
+    D = gemv.decode(enc)
+    inl = ~planted
+    assert np.all(np.abs(w - D)[inl] == dist.min(axis=2)[inl])
+    assert np.all(D[planted] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Pin 7: bit accounting against the pages' orders of magnitude
+# ---------------------------------------------------------------------------
+def test_extra_bits_per_weight_one_percent():
+    """[SpQR] about 1 % FP16 outliers + index overhead = roughly 0.5-1 extra bit per weight."""
+    for name, layer in [("tiny_u4", 0), ("block7b_u3", 0), ("block7b_u3", 6)]:
+        wl = WORKLOADS[name]
+        M, K = (wl.layers[layer][1:] if wl.layers else (wl.M, wl.K))
+        nnz = outlier_count(wl, M, K)
+        bpw = accounting.sparse_bpw(M, K, nnz)
+        assert 0.45 <= bpw <= 1.0, (name, bpw)
+    assert abs(accounting.sparse_bpw(512, 512, 2621) - 0.5425) < 1e-4
+
+
+def test_extra_bits_per_weight_squeezellm_order_of_magnitude():
+    """[SqLLM] ~0.45 % outliers cost about 0.1 bit/weight: same order of magnitude."""
+    wl = WORKLOADS["mlp7b_lut3"]
+    nnz = outlier_count(wl, wl.M, wl.K)
+    assert nnz == 202899
+    for col_bytes in (2, 4):
+        bpw = accounting.sparse_bpw(wl.M, wl.K, nnz, col_bytes=col_bytes)
+        assert 0.05 < bpw < 0.5
+    assert accounting.dense_bpw(3, "lut", 4096) == pytest.approx(3.03125)
+    assert accounting.dense_bpw(3, "uniform", 4096, 16) == 5.0
