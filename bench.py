@@ -1,0 +1,237 @@
+"""Benchmark of the batch-1 dense-and-sparse quantized GEMV on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step is one qgemv_run: decode of every packed code, fp32 dot with x, the
+CSR outlier SpMV into the same y, y written once.  Inputs are synthetic arrays
+in the storage format with the workload's shapes, code widths, FP16 tables and
+outlier structure, resident in HBM before timing starts.
+
+Distinct copies of the weight blob (>= 1 GiB in total) are cycled so that
+every step streams its weights from HBM rather than from the 256 MB
+last-level cache.  The timed region is one HIP-graph replay of exactly K
+launches, bracketed by device synchronisation and timed with HIP events on
+the launch stream.
+
+Prints ONE JSON line.  `value` is effective GB/s: algorithmic bytes per
+launch (packed codes, FP16 statistics or tables, CSR as FP16 value + int32
+column + int32 row pointer, x, y; each counted once) divided by the mean
+launch time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_NOTES = {
+    "mlp70b_lut4": "70B-shaped MLP 28672x8192, 4-bit codes + per-row FP16 LUT-16, 0.5% FP16 CSR outliers "
+                   "(5% of rows at 10x density + 2 full columns), batch 1",
+    "mlp7b_lut3": "MLP up-proj 11008x4096, 3-bit codes + per-row FP16 LUT-8, 0.45% FP16 CSR outliers, batch 1",
+    "attn7b_u3": "attention projection 4096x4096, 3-bit codes + FP16 scale/zero per 16, 0.5% FP16 CSR outliers, batch 1",
+    "tiny_u4": "512x512, 4-bit codes + FP16 scale/zero per 16, 1% FP16 CSR outliers, batch 1",
+    "block7b_u3": "7B down-proj 4096x11008, 3-bit codes + FP16 scale/zero per 16, 1% FP16 CSR outliers, batch 1",
+}
+
+
+def algorithmic_bytes(f: dict, B: int = 1) -> int:
+    M, K, bits = f["M"], f["K"], f["bits"]
+    nnz = int(f["row_ptr"][-1])
+    codes = M * K * bits // 8
+    meta = M * (K // 16) * 4 if f["fmt"] == "uniform" else M * (1 << bits) * 2
+    csr = 6 * nnz + 4 * (M + 1)
+    return codes + meta + csr + 2 * B * K + 4 * B * M
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "dense_sparse_bit_amd", "csrc")
+    for n in sorted(os.listdir(d)):
+        with open(os.path.join(d, n), "rb") as fh:
+            h.update(n.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_src_sha") != src_hash:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def csr_from_positions(M, rows, cols, values):
+    import numpy as np
+    counts = np.bincount(rows, minlength=M)
+    row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return row_ptr, cols.astype(np.int32), np.asarray(values, dtype=np.float16)
+
+
+def format_inputs(workload: str):
+    from synth import make_format_inputs
+    layer = 6 if workload == "block7b_u3" else 0
+    f = make_format_inputs(workload, layer)
+    f["row_ptr"], f["col_idx"], f["values"] = csr_from_positions(f["M"], f["rows"], f["cols"], f["values"])
+    return f, layer
+
+
+def cpu_baseline(f: dict, x16, alg_bytes: int, target_s: float = 12.0):
+    """The oracle's unpack + decode + GEMV + SpMV, single thread, on a bounded row sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gemv
+    M = f["M"]
+    rng = np.random.default_rng(7)
+    n = min(M, 1024)
+    rows = np.sort(rng.choice(M, size=n, replace=False))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        gemv.gemv_rows(f, x16, rows)
+        one = time.perf_counter() - t0
+        reps = max(1, min(20, int(target_s / max(one, 1e-3))))
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            gemv.gemv_rows(f, x16, rows)
+            ts.append(time.perf_counter() - t0)
+    t_rows = float(np.median(ts))
+    t_layer = t_rows * M / n
+    return {
+        "value": alg_bytes / t_layer / 1e9,
+        "unit": "GB/s",
+        "us_per_layer": t_layer * 1e6,
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} of {M} rows (random, seed 7), median of {reps} runs after 1 warm-up, "
+                  f"scaled by {M}/{n}; fp64 numpy, 1 thread; host CPU: {platform.processor() or platform.machine()}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="mlp70b_lut4", choices=sorted(WORKLOAD_NOTES))
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dense_sparse_bit_amd import qgemv
+    from synth import make_x
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    f, layer = format_inputs(a.workload)
+    M, K = f["M"], f["K"]
+    host_blob = qgemv.repack(f)
+    copies = max(1, math.ceil(a.rotate_gib * (1 << 30) / host_blob.size))
+    plans = [qgemv.QGemv(f, device="cuda:0", blob=host_blob) for _ in range(copies)]
+    x16 = make_x(a.workload, 1, K, layer, M)
+    x = torch.from_numpy(x16).to(dev)
+    ys = [torch.empty((1, M), dtype=torch.float32, device=dev) for _ in range(copies)]
+    alg = algorithmic_bytes(f)
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def launch(i):
+        plans[i % copies].run(x, ys[i % copies], stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(a.warmup):
+            launch(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not a.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(a.steps):
+                launch(i)
+        torch.cuda.synchronize()
+        graph.replay()  # warm the graph once (untimed)
+        torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(a.steps):
+                launch(i)
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / a.steps
+    us = ms_per_step * 1e3
+    gbs = alg / (ms_per_step * 1e-3) / 1e9
+
+    # every copy must have produced the same, finite y
+    y0 = ys[0].cpu().numpy()
+    assert np.all(np.isfinite(y0))
+    for y in ys[1:]:
+        assert np.array_equal(y.cpu().numpy(), y0)
+
+    src = kernel_source_hash()
+    traffic = load_traffic(a.workload, src)
+    out = {
+        "metric": "µs/layer and effective GB/s (batch-1 qGEMV) as % of MI355X HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "us_per_layer": round(us, 3),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": f"{a.workload}: {WORKLOAD_NOTES[a.workload]}", "M": M, "K": K,
+                   "bits": f["bits"], "format": f["fmt"], "batch": 1, "nnz": int(f["row_ptr"][-1]),
+                   "weight_copies_rotated": copies, "blob_bytes": int(host_blob.size),
+                   "timing": "eager launches" if graph is None else "one HIP-graph replay of all steps"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg, "kernel_src_sha": src},
+    }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(f, x16, alg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

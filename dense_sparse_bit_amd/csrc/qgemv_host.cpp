@@ -1,0 +1,326 @@
+// qgemv_host.cpp -- host side of the C ABI: validation, the offline repacker,
+// its host inverse, and status strings.  No GPU is touched here.
+
+#include <cmath>
+#include <cstring>
+
+#include "../../include/qgemv.h"
+#include "qgemv_internal.h"
+#include "qgemv_layout.h"
+
+using namespace qgemv_layout;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// IEEE binary16 bits -> float.
+float half_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  const int exp = (h >> 10) & 31;
+  const uint32_t man = h & 1023u;
+  float v;
+  if (exp == 0) {
+    v = std::ldexp((float)man, -24);
+  } else if (exp == 31) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = std::ldexp((float)(man | 1024u), exp - 25);
+  }
+  uint32_t bits;
+  std::memcpy(&bits, &v, 4);
+  bits |= sign;
+  std::memcpy(&v, &bits, 4);
+  return v;
+}
+
+bool half_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
+
+// Canonical LSB-first bitstream: code j of a row.
+inline uint32_t canon_get(const uint8_t* row, int j, int bits) {
+  uint32_t v = 0;
+  for (int t = 0; t < bits; ++t) {
+    const int p = j * bits + t;
+    v |= (uint32_t)((row[p >> 3] >> (p & 7)) & 1) << t;
+  }
+  return v;
+}
+
+inline void canon_put(uint8_t* row, int j, int bits, uint32_t code) {
+  for (int t = 0; t < bits; ++t) {
+    const int p = j * bits + t;
+    const uint8_t m = (uint8_t)(1u << (p & 7));
+    if ((code >> t) & 1)
+      row[p >> 3] |= m;
+    else
+      row[p >> 3] &= (uint8_t)~m;
+  }
+}
+
+// ---- chunk placement: 32 canonical codes <-> the kernel's dwords ----------
+
+void place_u4(const uint32_t* c, uint32_t* w) {
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
+    for (int t = 0; t < 4; ++t) {
+      const int m = 4 * d + t;
+      v |= c[2 * m] << (4 * t);
+      v |= c[2 * m + 1] << (16 + 4 * t);
+    }
+    w[d] = v;
+  }
+}
+
+void unplace_u4(const uint32_t* w, uint32_t* c) {
+  for (int d = 0; d < 4; ++d)
+    for (int t = 0; t < 4; ++t) {
+      const int m = 4 * d + t;
+      c[2 * m] = (w[d] >> (4 * t)) & 15u;
+      c[2 * m + 1] = (w[d] >> (16 + 4 * t)) & 15u;
+    }
+}
+
+constexpr int kU3Shift[5] = {0, 3, 6, 10, 13};
+
+void place_u3(const uint32_t* c, uint32_t* w) {
+  for (int d = 0; d < 3; ++d) {
+    uint32_t v = 0;
+    for (int t = 0; t < 5; ++t) {
+      const int m = 5 * d + t;
+      v |= c[2 * m] << kU3Shift[t];
+      v |= c[2 * m + 1] << (16 + kU3Shift[t]);
+    }
+    // pair 15: one bit of each of its two codes per dword
+    v |= ((c[30] >> d) & 1u) << 9;
+    v |= ((c[31] >> d) & 1u) << 25;
+    w[d] = v;
+  }
+}
+
+void unplace_u3(const uint32_t* w, uint32_t* c) {
+  for (int d = 0; d < 3; ++d)
+    for (int t = 0; t < 5; ++t) {
+      const int m = 5 * d + t;
+      c[2 * m] = (w[d] >> kU3Shift[t]) & 7u;
+      c[2 * m + 1] = (w[d] >> (16 + kU3Shift[t])) & 7u;
+    }
+  c[30] = c[31] = 0;
+  for (int d = 0; d < 3; ++d) {
+    c[30] |= ((w[d] >> 9) & 1u) << d;
+    c[31] |= ((w[d] >> 25) & 1u) << d;
+  }
+}
+
+void place_l4(const uint32_t* c, uint32_t* w) {
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = c[8 * d + k], b = c[8 * d + 4 + k];
+      const uint32_t byte = (a & 7u) | ((b & 7u) << 3) | ((a >> 3) << 6) | ((b >> 3) << 7);
+      v |= byte << (8 * k);
+    }
+    w[d] = v;
+  }
+}
+
+void unplace_l4(const uint32_t* w, uint32_t* c) {
+  for (int d = 0; d < 4; ++d)
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t byte = (w[d] >> (8 * k)) & 255u;
+      c[8 * d + k] = (byte & 7u) | (((byte >> 6) & 1u) << 3);
+      c[8 * d + 4 + k] = ((byte >> 3) & 7u) | (((byte >> 7) & 1u) << 3);
+    }
+}
+
+void place_l3(const uint32_t* c, uint32_t* w) {
+  for (int d = 0; d < 3; ++d) {
+    uint32_t v = 0;
+    for (int k = 0; k < 4; ++k) {
+      uint32_t byte = (c[8 * d + k] & 7u) | ((c[8 * d + 4 + k] & 7u) << 3);
+      if (d == 0) byte |= (c[24 + k] & 3u) << 6;
+      if (d == 1) byte |= (c[28 + k] & 3u) << 6;
+      if (d == 2) byte |= ((c[24 + k] >> 2) << 6) | ((c[28 + k] >> 2) << 7);
+      v |= byte << (8 * k);
+    }
+    w[d] = v;
+  }
+}
+
+void unplace_l3(const uint32_t* w, uint32_t* c) {
+  for (int d = 0; d < 3; ++d)
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t byte = (w[d] >> (8 * k)) & 255u;
+      c[8 * d + k] = byte & 7u;
+      c[8 * d + 4 + k] = (byte >> 3) & 7u;
+    }
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b0 = (w[0] >> (8 * k)) & 255u, b1 = (w[1] >> (8 * k)) & 255u,
+                   b2 = (w[2] >> (8 * k)) & 255u;
+    c[24 + k] = ((b0 >> 6) & 3u) | (((b2 >> 6) & 1u) << 2);
+    c[28 + k] = ((b1 >> 6) & 3u) | (((b2 >> 7) & 1u) << 2);
+  }
+}
+
+void place_chunk(int bits, int format, const uint32_t* c, uint32_t* w) {
+  if (format == QGEMV_FMT_UNIFORM)
+    bits == 4 ? place_u4(c, w) : place_u3(c, w);
+  else
+    bits == 4 ? place_l4(c, w) : place_l3(c, w);
+}
+
+void unplace_chunk(int bits, int format, const uint32_t* w, uint32_t* c) {
+  if (format == QGEMV_FMT_UNIFORM)
+    bits == 4 ? unplace_u4(w, c) : unplace_u3(w, c);
+  else
+    bits == 4 ? unplace_l4(w, c) : unplace_l3(w, c);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Validation shared by the entry points
+// ---------------------------------------------------------------------------
+int qgemv_validate_shape(const qgemv_weights* w) {
+  if (!w) return QGEMV_ERR_INVALID_ARG;
+  if (w->M < 1 || w->K < 1 || w->nnz < 0) return QGEMV_ERR_INVALID_ARG;
+  if (w->bits != 3 && w->bits != 4) return QGEMV_ERR_UNSUPPORTED;
+  if (w->format != QGEMV_FMT_UNIFORM && w->format != QGEMV_FMT_LUT) return QGEMV_ERR_UNSUPPORTED;
+  if (w->K % kChunkCodes != 0 || w->K > kMaxK) return QGEMV_ERR_UNSUPPORTED;
+  if (w->format == QGEMV_FMT_UNIFORM && w->group_size != 16) return QGEMV_ERR_UNSUPPORTED;
+  if (w->nnz > 0x7fffffffLL) return QGEMV_ERR_UNSUPPORTED;
+  if ((int64_t)w->M * w->K > ((int64_t)1 << 40)) return QGEMV_ERR_UNSUPPORTED;
+  return QGEMV_OK;
+}
+
+static int validate_arrays(const qgemv_weights* w) {
+  int st = qgemv_validate_shape(w);
+  if (st) return st;
+  const int64_t M = w->M, K = w->K, nnz = w->nnz;
+  if (!w->codes || !w->row_ptr) return QGEMV_ERR_INVALID_ARG;
+  if (nnz > 0 && (!w->col_idx || !w->values)) return QGEMV_ERR_INVALID_ARG;
+  const int L = (1 << w->bits) - 1;
+  if (w->format == QGEMV_FMT_UNIFORM) {
+    if (!w->scales || !w->zeros) return QGEMV_ERR_INVALID_ARG;
+    const int64_t n = M * (K / w->group_size);
+    for (int64_t i = 0; i < n; ++i) {
+      if (!half_finite(w->scales[i])) return QGEMV_ERR_INVALID_ARG;
+      const float z = half_to_float(w->zeros[i]);
+      if (!(z >= 0.0f && z <= (float)L && z == std::floor(z))) return QGEMV_ERR_INVALID_ARG;
+    }
+  } else {
+    if (!w->lut) return QGEMV_ERR_INVALID_ARG;
+    const int64_t n = M << w->bits;
+    for (int64_t i = 0; i < n; ++i)
+      if (!half_finite(w->lut[i])) return QGEMV_ERR_INVALID_ARG;
+  }
+  if (w->row_ptr[0] != 0 || (int64_t)w->row_ptr[M] != nnz) return QGEMV_ERR_MALFORMED_CSR;
+  for (int64_t i = 0; i < M; ++i) {
+    const int32_t a = w->row_ptr[i], b = w->row_ptr[i + 1];
+    if (b < a || a < 0 || (int64_t)b > nnz) return QGEMV_ERR_MALFORMED_CSR;
+    for (int32_t p = a; p < b; ++p) {
+      const int32_t c = w->col_idx[p];
+      if (c < 0 || c >= K) return QGEMV_ERR_MALFORMED_CSR;
+      if (p > a && c <= w->col_idx[p - 1]) return QGEMV_ERR_MALFORMED_CSR;
+      if (!half_finite(w->values[p])) return QGEMV_ERR_INVALID_ARG;
+    }
+  }
+  return QGEMV_OK;
+}
+
+void qgemv_set_hip_error(int e) { g_last_hip_error = e; }
+
+extern "C" {
+
+int qgemv_packed_size(const qgemv_weights* w, size_t* bytes) {
+  if (!bytes) return QGEMV_ERR_INVALID_ARG;
+  const int st = validate_arrays(w);
+  if (st) return st;
+  *bytes = (size_t)make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz).total_bytes;
+  return QGEMV_OK;
+}
+
+int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
+  if (!dst_host) return QGEMV_ERR_INVALID_ARG;
+  const int st = validate_arrays(w);
+  if (st) return st;
+  const BlobHeader h = make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz);
+  if (bytes < h.total_bytes) return QGEMV_ERR_SIZE;
+  uint8_t* blob = (uint8_t*)dst_host;
+  std::memset(blob, 0, (size_t)h.total_bytes);
+  std::memcpy(blob, &h, sizeof(h));
+
+  const int M = w->M, K = w->K, bits = w->bits;
+  const int chunks = K / kChunkCodes;
+  const int chunk_bytes = 4 * bits;
+  uint32_t c[32], dw[4];
+  for (int i = 0; i < M; ++i) {
+    const uint8_t* src = w->codes + (size_t)i * h.row_bytes;
+    uint8_t* dst = blob + h.off_codes + (size_t)i * h.row_bytes;
+    for (int ch = 0; ch < chunks; ++ch) {
+      for (int j = 0; j < 32; ++j) c[j] = canon_get(src, ch * 32 + j, bits);
+      place_chunk(bits, w->format, c, dw);
+      std::memcpy(dst + (size_t)ch * chunk_bytes, dw, chunk_bytes);
+    }
+  }
+
+  uint8_t* meta = blob + h.off_meta;
+  if (w->format == QGEMV_FMT_UNIFORM) {
+    const int64_t n = (int64_t)M * (K / w->group_size);
+    uint32_t* m32 = (uint32_t*)meta;
+    for (int64_t g = 0; g < n; ++g) m32[g] = (uint32_t)w->scales[g] | ((uint32_t)w->zeros[g] << 16);
+  } else {
+    const int E = 1 << bits;
+    for (int i = 0; i < M; ++i) {
+      const uint16_t* t = w->lut + (size_t)i * E;
+      uint8_t* r = meta + (size_t)i * h.meta_row_bytes;
+      for (int e = 0; e < E; ++e) {
+        r[e] = (uint8_t)(t[e] & 255u);      // lo-byte plane
+        r[E + e] = (uint8_t)(t[e] >> 8);    // hi-byte plane
+      }
+    }
+  }
+
+  std::memcpy(blob + h.off_rowptr, w->row_ptr, 4ull * ((size_t)M + 1));
+  uint32_t* ent = (uint32_t*)(blob + h.off_entries);
+  for (int64_t p = 0; p < w->nnz; ++p)
+    ent[p] = (uint32_t)w->col_idx[p] | ((uint32_t)w->values[p] << 16);
+  return QGEMV_OK;
+}
+
+int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out) {
+  if (!blob_host || !codes_out) return QGEMV_ERR_INVALID_ARG;
+  if (bytes < sizeof(BlobHeader)) return QGEMV_ERR_SIZE;
+  BlobHeader h;
+  std::memcpy(&h, blob_host, sizeof(h));
+  if (h.magic != kMagic || h.version != kVersion) return QGEMV_ERR_SIZE;
+  if (h.total_bytes > bytes) return QGEMV_ERR_SIZE;
+  const uint8_t* blob = (const uint8_t*)blob_host;
+  const int chunks = h.K / kChunkCodes, chunk_bytes = 4 * h.bits;
+  uint32_t c[32], dw[4];
+  for (int i = 0; i < h.M; ++i) {
+    const uint8_t* src = blob + h.off_codes + (size_t)i * h.row_bytes;
+    uint8_t* dst = codes_out + (size_t)i * h.K;
+    for (int ch = 0; ch < chunks; ++ch) {
+      std::memcpy(dw, src + (size_t)ch * chunk_bytes, chunk_bytes);
+      unplace_chunk(h.bits, h.format, dw, c);
+      for (int j = 0; j < 32; ++j) dst[ch * 32 + j] = (uint8_t)c[j];
+    }
+  }
+  return QGEMV_OK;
+}
+
+const char* qgemv_error_string(int status) {
+  switch (status) {
+    case QGEMV_OK: return "ok";
+    case QGEMV_ERR_INVALID_ARG: return "invalid argument";
+    case QGEMV_ERR_MALFORMED_CSR: return "malformed CSR (row_ptr/col_idx)";
+    case QGEMV_ERR_UNSUPPORTED: return "unsupported bits/format/group/K/batch";
+    case QGEMV_ERR_HIP: return "HIP runtime error";
+    case QGEMV_ERR_SIZE: return "buffer too small or blob header mismatch";
+    default: return "unknown status";
+  }
+}
+
+int qgemv_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+/*
+ * qgemv.h -- dense-and-sparse quantized matrix-vector product for MI355X (gfx950).
+ *
+ *   y[b][i] = sum_j dequant(W_dense)[i][j] * x[b][j]  +  sum_{p in row i} values[p] * x[b][col_idx[p]]
+ *
+ * The operation is the dense-and-sparse decomposition W = W_dense + W_sparse of
+ * the page "SqueezeLLM (Dense-and-Sparse Quantization)", section
+ * "2. Dense-and-Sparse decomposition", applied to an activation vector.  The
+ * dense part holds 3- or 4-bit codes; they decode either through an FP16
+ * (scale, zero) pair per group of 16 weights along K (page "SpQR
+ * (Sparse-Quantized Representation)", section "Quantification d'un modèle":
+ * wbits 3, groupsize 16) or through a per-output-row FP16 lookup table of
+ * 2^bits entries (SqueezeLLM page, section "Non-uniform quantization via
+ * Lloyd-Max optimisé").  The sparse part holds FP16 outliers in CSR form
+ * (SpQR page, section "Le format de stockage sparse": values FP16, col_idx,
+ * row_ptr).
+ *
+ * Flow: qgemv_packed_size + qgemv_repack (host, offline) turn the canonical
+ * arrays below into one self-describing blob laid out for the gfx950 kernels;
+ * the caller copies the blob to device memory it owns; qgemv_create binds a
+ * plan to it; qgemv_run enqueues the product on a HIP stream.
+ *
+ * Every entry point returns an int status: QGEMV_OK (0) or a negative
+ * qgemv_status.  No entry point aborts, throws or prints.  All entry points
+ * are thread-safe; runs of one plan on different streams with distinct y
+ * buffers may overlap.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QGEMV_OK = 0,
+  QGEMV_ERR_INVALID_ARG = -1,   /* null pointer, bad alignment, inconsistent sizes      */
+  QGEMV_ERR_MALFORMED_CSR = -2, /* row_ptr not monotone / not ending at nnz, col out of
+                                   range or not strictly ascending within a row          */
+  QGEMV_ERR_UNSUPPORTED = -3,   /* bits, format, group size, K or batch outside the
+                                   supported set (see qgemv_weights and qgemv_run)      */
+  QGEMV_ERR_HIP = -4,           /* a HIP runtime call failed; qgemv_last_hip_error()
+                                   returns its hipError_t value                          */
+  QGEMV_ERR_SIZE = -5           /* destination / blob buffer too small, or the blob
+                                   header does not match the descriptor                  */
+} qgemv_status;
+
+typedef enum {
+  QGEMV_FMT_UNIFORM = 0, /* d = scale[i][g] * (q - zero[i][g]),  g = j / group_size */
+  QGEMV_FMT_LUT = 1      /* d = lut[i][q]                                            */
+} qgemv_format;
+
+/*
+ * Canonical ("the pages'") weight format.  All arrays are host memory,
+ * little-endian, row-major, borrowed for the duration of the call only.
+ *
+ *   M, K        W is M x K (out x in).  K % 32 == 0, 32 <= K <= 16384, M >= 1.
+ *   bits        3 or 4.
+ *   format      qgemv_format.
+ *   group_size  16 for QGEMV_FMT_UNIFORM (groups run along K); ignored for LUT.
+ *   nnz         number of CSR entries, >= 0.
+ *   codes       uint8 [M][K*bits/8]: row i is one contiguous bitstream starting
+ *               at byte i*K*bits/8; code j occupies bits [j*bits, j*bits+bits),
+ *               least significant bit first.
+ *   scales      FP16 bits [M][K/group_size] (UNIFORM), else NULL.  Finite.
+ *   zeros       FP16 bits [M][K/group_size] (UNIFORM), else NULL.  Integer
+ *               valued in [0, 2^bits - 1].
+ *   lut         FP16 bits [M][2^bits] (LUT), else NULL.  Finite.
+ *   row_ptr     int32 [M+1]: row_ptr[0] = 0, non-decreasing, row_ptr[M] = nnz.
+ *   col_idx     int32 [nnz]: 0 <= c < K, strictly ascending inside a row.
+ *   values      FP16 bits [nnz], finite.  col_idx/values may be NULL iff nnz == 0.
+ */
+typedef struct {
+  int32_t M, K;
+  int32_t bits;
+  int32_t format;
+  int32_t group_size;
+  int64_t nnz;
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  const uint16_t* lut;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const uint16_t* values;
+} qgemv_weights;
+
+typedef struct qgemv_plan* qgemv_handle;
+
+/*
+ * Validate w (every array, see qgemv_weights) and report the size in bytes of
+ * the repacked blob.  Host only; touches no GPU.
+ * Errors: INVALID_ARG (null w/bytes, null array, negative nnz), UNSUPPORTED,
+ * MALFORMED_CSR.
+ */
+int qgemv_packed_size(const qgemv_weights* w, size_t* bytes);
+
+/*
+ * Validate w and write the gfx950 blob into dst_host (host memory of at least
+ * qgemv_packed_size bytes).  Host only.  The blob is a pure function of w.
+ * Errors: as qgemv_packed_size, plus SIZE when bytes is too small.
+ */
+int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes);
+
+/*
+ * Host-side inverse of the code repacking: read a blob in host memory and
+ * write the canonical codes, one uint8 per weight, to codes_out [M][K] (host).
+ * For tests of the repacker without a GPU.
+ * Errors: INVALID_ARG (null pointer), SIZE (blob shorter than its header says
+ * or header not recognised).
+ */
+int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out);
+
+/*
+ * Bind a plan to a blob already copied to device memory (packed_dev, bytes,
+ * 256-byte aligned).  shape supplies M, K, bits, format, group_size and nnz;
+ * its array pointers are ignored.  The blob's header is read back once
+ * (synchronous device-to-host copy) and must match shape.  The caller keeps
+ * the blob alive and unmodified until qgemv_destroy.  The plan allocates no
+ * device memory.
+ * Errors: INVALID_ARG, UNSUPPORTED, SIZE (bytes too small or header mismatch),
+ * HIP.
+ */
+int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* packed_dev, size_t bytes);
+
+/*
+ * Enqueue y = dequant(W_dense) x + W_sparse x on `stream` (a hipStream_t; NULL
+ * = the default stream).  x_dev: FP16 [batch][K] device memory, 16-byte
+ * aligned, contiguous.  y_dev: fp32 [batch][M] device memory, 16-byte
+ * aligned; every element is overwritten.  batch must be 1, 8 or 16.
+ * Asynchronous: errors of the running kernel surface at the caller's next
+ * synchronisation.
+ * Errors: INVALID_ARG (null handle/pointer, misalignment), UNSUPPORTED (batch),
+ * HIP (launch failure).
+ */
+int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, void* stream);
+
+/*
+ * Enqueue a kernel that decodes the blob's codes back to canonical order, one
+ * uint8 per weight, into codes_dev [M][K] (device memory).  Uses the same
+ * unpacking as the product kernels; for bit-exact checks of the codes.
+ * Errors: INVALID_ARG, HIP.
+ */
+int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream);
+
+/* Release the plan (host memory only).  NULL is accepted. */
+int qgemv_destroy(qgemv_handle h);
+
+/* Static description of a status code; never NULL. */
+const char* qgemv_error_string(int status);
+
+/* hipError_t of the most recent QGEMV_ERR_HIP on the calling thread (0 if none). */
+int qgemv_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,184 @@
+"""Host-side checks of the C ABI: exported symbols, validation, and the repacker.
+
+No GPU is needed: only qgemv_packed_size / qgemv_repack / qgemv_unpack_host /
+qgemv_error_string and argument checks that fail before any HIP call run here.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from dense_sparse_bit_amd import qgemv
+from oracle import encode, pack
+from synth import WORKLOADS, make_weights, make_x, outlier_count
+
+
+def test_library_exports_every_declared_symbol():
+    L = qgemv.lib()
+    names = qgemv.header_symbols()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_error_strings():
+    L = qgemv.lib()
+    for st in [0, -1, -2, -3, -4, -5, 7]:
+        s = L.qgemv_error_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert L.qgemv_error_string(0) == b"ok"
+    assert L.qgemv_last_hip_error() == 0
+
+
+def _random_canonical(fmt, bits, M, K, nnz_per_row=3, seed=0):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 1 << bits, size=(M, K)).astype(np.uint8)
+    w = {"M": M, "K": K, "bits": bits, "fmt": fmt, "group": 16 if fmt == "uniform" else 0,
+         "codes": codes, "codes_packed": pack.pack_bitstream(codes, bits)}
+    if fmt == "uniform":
+        w["scales"] = rng.uniform(1e-3, 2e-2, size=(M, K // 16)).astype(np.float16)
+        w["zeros"] = rng.integers(0, 1 << bits, size=(M, K // 16)).astype(np.float16)
+    else:
+        w["lut"] = np.sort(rng.standard_normal((M, 1 << bits)) * 0.05, axis=1).astype(np.float16)
+    cols = [np.sort(rng.choice(K, size=min(K, nnz_per_row), replace=False)) for _ in range(M)]
+    w["row_ptr"] = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    w["col_idx"] = np.concatenate(cols).astype(np.int32)
+    w["values"] = rng.uniform(-2, 2, size=len(w["col_idx"])).astype(np.float16)
+    return w
+
+
+FORMATS = [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4)]
+
+
+@pytest.mark.parametrize("fmt,bits", FORMATS)
+@pytest.mark.parametrize("K", [32, 64, 2048, 2080, 4128, 11008])
+def test_repack_roundtrip_random(fmt, bits, K):
+    w = _random_canonical(fmt, bits, 5, K, seed=K + bits)
+    blob = qgemv.repack(w)
+    assert blob.size == qgemv.packed_size(w)
+    assert blob.size % 256 == 0
+    assert np.array_equal(qgemv.unpack_host(blob, 5, K), w["codes"])
+    assert np.array_equal(qgemv.repack(w), blob)   # deterministic
+
+
+@pytest.mark.parametrize("fmt,bits", FORMATS)
+def test_repack_roundtrip_every_code_value_in_every_slot(fmt, bits):
+    K = 32 * (1 << bits)
+    codes = np.array([[(j + r) % (1 << bits) for j in range(K)] for r in range(1 << bits)], dtype=np.uint8)
+    w = _random_canonical(fmt, bits, codes.shape[0], K)
+    w["codes"], w["codes_packed"] = codes, pack.pack_bitstream(codes, bits)
+    assert np.array_equal(qgemv.unpack_host(qgemv.repack(w), codes.shape[0], K), codes)
+
+
+@pytest.mark.parametrize("name,M,K", [("tiny_u4", None, None), ("attn7b_u3", 40, 2080),
+                                      ("mlp7b_lut3", 12, 4096), ("mlp70b_lut4", 6, 4128)])
+def test_repack_roundtrip_oracle_encoding(name, M, K):
+    wl = WORKLOADS[name]
+    W, planted = make_weights(wl, 0, M, K)
+    M, K = W.shape
+    x = make_x(wl, 1, K, 0, M)
+    enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M, K), 16, sens=x[0].astype(np.float64) ** 2)
+    blob = qgemv.repack(enc)
+    assert np.array_equal(qgemv.unpack_host(blob, M, K), enc["codes"])
+    # header, row_ptr and entries sections
+    hdr = blob[:256].view(np.uint32)
+    assert hdr[0] == 0x564D4751 and hdr[2] == M and hdr[3] == K and hdr[4] == wl.bits
+    off = blob[:256].view(np.uint64)
+    nnz = int(blob[32:40].view(np.int64)[0])
+    assert nnz == enc["row_ptr"][-1]
+    off_rowptr, off_entries = int(off[7]), int(off[8])
+    assert np.array_equal(blob[off_rowptr:off_rowptr + 4 * (M + 1)].view(np.int32), enc["row_ptr"])
+    ent = blob[off_entries:off_entries + 4 * nnz].view(np.uint32)
+    assert np.array_equal(ent & 0xFFFF, enc["col_idx"])
+    assert np.array_equal((ent >> 16).astype(np.uint16), enc["values"].view(np.uint16))
+
+
+def _status(w):
+    try:
+        qgemv.packed_size(w)
+        return 0
+    except qgemv.QgemvError as e:
+        return e.status
+
+
+def test_validation_errors():
+    base = _random_canonical("uniform", 4, 4, 64)
+    assert _status(base) == 0
+    INV, CSR, UNS = -1, -2, -3
+
+    def mod(**kw):
+        w = dict(base)
+        w.update(kw)
+        return w
+    assert _status(mod(bits=5)) == UNS
+    assert _status(mod(bits=2)) == UNS
+    assert _status(mod(fmt=7)) == UNS
+    assert _status(mod(group=32)) == UNS
+    assert _status(mod(K=48, codes_packed=base["codes_packed"])) == UNS
+    assert _status(mod(M=0)) == INV
+    assert _status(mod(codes_packed=None)) == INV
+    rp = base["row_ptr"].copy(); rp[0] = 1
+    assert _status(mod(row_ptr=rp, nnz=int(base["row_ptr"][-1]))) == CSR
+    rp = base["row_ptr"].copy(); rp[2], rp[1] = rp[1], rp[2]
+    assert _status(mod(row_ptr=rp)) == CSR
+    ci = base["col_idx"].copy(); ci[0] = 64
+    assert _status(mod(col_idx=ci)) == CSR
+    ci = base["col_idx"].copy(); ci[1] = ci[0]
+    assert _status(mod(col_idx=ci)) == CSR
+    ci = base["col_idx"].copy(); ci[0] = -1
+    assert _status(mod(col_idx=ci)) == CSR
+    z = base["zeros"].copy(); z[0, 0] = 16
+    assert _status(mod(zeros=z)) == INV
+    z = base["zeros"].copy(); z[0, 0] = 1.5
+    assert _status(mod(zeros=z)) == INV
+    s = base["scales"].copy(); s[0, 0] = np.nan
+    assert _status(mod(scales=s)) == INV
+    v = base["values"].copy(); v[0] = np.inf
+    assert _status(mod(values=v)) == INV
+    lw = _random_canonical("lut", 3, 4, 64)
+    lut = lw["lut"].copy(); lut[1, 2] = np.inf
+    w = dict(lw); w["lut"] = lut
+    assert _status(w) == INV
+    w = dict(lw); w["lut"] = None
+    assert _status(w) == INV
+    big = _random_canonical("lut", 4, 1, 32)
+    big["K"] = 16384 + 32
+    assert _status(big) == UNS
+
+
+def test_nnz_mismatch_and_small_buffers():
+    w = _random_canonical("lut", 4, 3, 64)
+    w2 = dict(w); w2["nnz"] = int(w["row_ptr"][-1]) + 1
+    assert _status(w2) == -2
+    s, keep = qgemv.make_weights(w)
+    n = qgemv.packed_size(w)
+    buf = np.zeros(n - 1, dtype=np.uint8)
+    assert qgemv.lib().qgemv_repack(ctypes.byref(s), buf.ctypes.data, n - 1) == -5
+    assert qgemv.lib().qgemv_repack(ctypes.byref(s), None, n) == -1
+    assert qgemv.lib().qgemv_packed_size(None, None) == -1
+
+
+def test_unpack_host_rejects_garbage():
+    junk = np.zeros(512, dtype=np.uint8)
+    out = np.zeros(16, dtype=np.uint8)
+    assert qgemv.lib().qgemv_unpack_host(junk.ctypes.data, junk.size, out.ctypes.data) == -5
+    assert qgemv.lib().qgemv_unpack_host(None, 0, out.ctypes.data) == -1
+    w = _random_canonical("uniform", 3, 2, 64)
+    blob = qgemv.repack(w)
+    assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size - 256, out.ctypes.data) == -5
+
+
+def test_run_and_create_argument_checks_need_no_gpu():
+    L = qgemv.lib()
+    assert L.qgemv_run(None, None, None, 1, None) == -1
+    assert L.qgemv_debug_unpack(None, None, None) == -1
+    assert L.qgemv_destroy(None) == 0
+    h = ctypes.c_void_p(0)
+    assert L.qgemv_create(ctypes.byref(h), None, None, 0) == -1
+    w = _random_canonical("lut", 4, 3, 64)
+    s, keep = qgemv.make_weights(w)
+    # misaligned device pointer is rejected before any HIP call
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(s), ctypes.c_void_p(0x1001), 1 << 20) == -1
+    # a blob smaller than the descriptor needs is rejected before any HIP call
+    assert L.qgemv_create(ctypes.byref(h), ctypes.byref(s), ctypes.c_void_p(0x100000), 256) == -5
