@@ -152,7 +152,7 @@ def main():
     f, layer = format_inputs(a.workload)
     M, K = f["M"], f["K"]
     host_blob = qgemv.repack(f)
-    copies = max(1, math.ceil(a.rotate_gib * (1 << 30) / host_blob.size))
+    copies = max(1, min(a.steps, 256, math.ceil(a.rotate_gib * (1 << 30) / host_blob.size)))
     plans = [qgemv.QGemv(f, device="cuda:0", blob=host_blob) for _ in range(copies)]
     x16 = make_x(a.workload, 1, K, layer, M)
     x = torch.from_numpy(x16).to(dev)

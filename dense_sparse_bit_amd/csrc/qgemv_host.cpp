@@ -1,8 +1,10 @@
 // qgemv_host.cpp -- host side of the C ABI: validation, the offline repacker,
 // its host inverse, and status strings.  No GPU is touched here.
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "../../include/qgemv.h"
 #include "qgemv_internal.h"
@@ -36,24 +38,20 @@ float half_to_float(uint16_t h) {
 
 bool half_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
 
-// Canonical LSB-first bitstream: code j of a row.
-inline uint32_t canon_get(const uint8_t* row, int j, int bits) {
-  uint32_t v = 0;
-  for (int t = 0; t < bits; ++t) {
-    const int p = j * bits + t;
-    v |= (uint32_t)((row[p >> 3] >> (p & 7)) & 1) << t;
+// All K codes of one canonical row into out[0..K) (one byte each).
+void canon_unpack_row(const uint8_t* row, int K, int bits, uint8_t* out) {
+  if (bits == 4) {
+    for (int j = 0; j < K; j += 2) {
+      out[j] = row[j >> 1] & 15u;
+      out[j + 1] = row[j >> 1] >> 4;
+    }
+    return;
   }
-  return v;
-}
-
-inline void canon_put(uint8_t* row, int j, int bits, uint32_t code) {
-  for (int t = 0; t < bits; ++t) {
-    const int p = j * bits + t;
-    const uint8_t m = (uint8_t)(1u << (p & 7));
-    if ((code >> t) & 1)
-      row[p >> 3] |= m;
-    else
-      row[p >> 3] &= (uint8_t)~m;
+  // 3 bits: every 3 bytes hold 8 codes
+  for (int j = 0; j < K; j += 8) {
+    const uint8_t* p = row + 3 * (j / 8);
+    const uint32_t v = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+    for (int q = 0; q < 8; ++q) out[j + q] = (uint8_t)((v >> (3 * q)) & 7u);
   }
 }
 
@@ -187,8 +185,11 @@ int qgemv_validate_shape(const qgemv_weights* w) {
   if (w->format != QGEMV_FMT_UNIFORM && w->format != QGEMV_FMT_LUT) return QGEMV_ERR_UNSUPPORTED;
   if (w->K % kChunkCodes != 0 || w->K > kMaxK) return QGEMV_ERR_UNSUPPORTED;
   if (w->format == QGEMV_FMT_UNIFORM && w->group_size != 16) return QGEMV_ERR_UNSUPPORTED;
-  if (w->nnz > 0x7fffffffLL) return QGEMV_ERR_UNSUPPORTED;
+  if (w->nnz > 0x1fffffffLL) return QGEMV_ERR_UNSUPPORTED;  // byte offsets of entries stay in int32
   if ((int64_t)w->M * w->K > ((int64_t)1 << 40)) return QGEMV_ERR_UNSUPPORTED;
+  // the kernels address every section with 31-bit byte offsets
+  const BlobHeader h = make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz);
+  if (h.total_bytes >= ((uint64_t)1 << 31)) return QGEMV_ERR_UNSUPPORTED;
   return QGEMV_OK;
 }
 
@@ -204,6 +205,7 @@ static int validate_arrays(const qgemv_weights* w) {
     const int64_t n = M * (K / w->group_size);
     for (int64_t i = 0; i < n; ++i) {
       if (!half_finite(w->scales[i])) return QGEMV_ERR_INVALID_ARG;
+      if (std::fabs(half_to_float(w->scales[i])) * (float)L > 65504.0f) return QGEMV_ERR_UNSUPPORTED;
       const float z = half_to_float(w->zeros[i]);
       if (!(z >= 0.0f && z <= (float)L && z == std::floor(z))) return QGEMV_ERR_INVALID_ARG;
     }
@@ -249,35 +251,52 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
   std::memset(blob, 0, (size_t)h.total_bytes);
   std::memcpy(blob, &h, sizeof(h));
 
-  const int M = w->M, K = w->K, bits = w->bits;
-  const int chunks = K / kChunkCodes;
+  const int M = w->M, K = w->K, bits = w->bits, Kp = h.Kp, nkb = h.nkb;
+  const size_t row_bytes = (size_t)K * bits / 8;
   const int chunk_bytes = 4 * bits;
+  std::vector<uint8_t> tile((size_t)kTileRows * Kp);   // canonical codes of one tile, zero padded
   uint32_t c[32], dw[4];
-  for (int i = 0; i < M; ++i) {
-    const uint8_t* src = w->codes + (size_t)i * h.row_bytes;
-    uint8_t* dst = blob + h.off_codes + (size_t)i * h.row_bytes;
-    for (int ch = 0; ch < chunks; ++ch) {
-      for (int j = 0; j < 32; ++j) c[j] = canon_get(src, ch * 32 + j, bits);
-      place_chunk(bits, w->format, c, dw);
-      std::memcpy(dst + (size_t)ch * chunk_bytes, dw, chunk_bytes);
+  for (int t = 0; t < h.tiles; ++t) {
+    std::fill(tile.begin(), tile.end(), (uint8_t)0);
+    for (int r = 0; r < kTileRows; ++r) {
+      const int row = t * kTileRows + r;
+      if (row >= M) break;
+      canon_unpack_row(w->codes + (size_t)row * row_bytes, K, bits, tile.data() + (size_t)r * Kp);
+    }
+    for (int b = 0; b < nkb; ++b) {
+      uint8_t* dst = blob + h.off_codes + ((size_t)t * nkb + b) * h.block_bytes;
+      for (int l = 0; l < 64; ++l) {
+        const uint8_t* src = tile.data() + (size_t)(l % 16) * Kp + b * kBlockK + 32 * (l / 16);
+        for (int j = 0; j < 32; ++j) c[j] = src[j];
+        place_chunk(bits, w->format, c, dw);
+        std::memcpy(dst + (size_t)l * chunk_bytes, dw, chunk_bytes);
+      }
     }
   }
 
   uint8_t* meta = blob + h.off_meta;
   if (w->format == QGEMV_FMT_UNIFORM) {
-    const int64_t n = (int64_t)M * (K / w->group_size);
-    uint32_t* m32 = (uint32_t*)meta;
-    for (int64_t g = 0; g < n; ++g) m32[g] = (uint32_t)w->scales[g] | ((uint32_t)w->zeros[g] << 16);
+    const int G = K / w->group_size;
+    for (int t = 0; t < h.tiles; ++t)
+      for (int b = 0; b < nkb; ++b) {
+        uint32_t* m32 = (uint32_t*)(meta + ((size_t)t * nkb + b) * h.meta_unit_bytes);
+        for (int l = 0; l < 64; ++l) {
+          const int row = t * kTileRows + l % 16;
+          for (int q = 0; q < 2; ++q) {
+            const int g = (b * kBlockK + 32 * (l / 16)) / 16 + q;
+            uint32_t v = 0;
+            if (row < M && g < G) {
+              const size_t gi = (size_t)row * G + g;
+              v = (uint32_t)w->scales[gi] | ((uint32_t)w->zeros[gi] << 16);
+            }
+            m32[2 * l + q] = v;
+          }
+        }
+      }
   } else {
     const int E = 1 << bits;
-    for (int i = 0; i < M; ++i) {
-      const uint16_t* t = w->lut + (size_t)i * E;
-      uint8_t* r = meta + (size_t)i * h.meta_row_bytes;
-      for (int e = 0; e < E; ++e) {
-        r[e] = (uint8_t)(t[e] & 255u);      // lo-byte plane
-        r[E + e] = (uint8_t)(t[e] >> 8);    // hi-byte plane
-      }
-    }
+    for (int i = 0; i < M; ++i)
+      std::memcpy(meta + (size_t)i * h.meta_unit_bytes, w->lut + (size_t)i * E, 2 * (size_t)E);
   }
 
   std::memcpy(blob + h.off_rowptr, w->row_ptr, 4ull * ((size_t)M + 1));
@@ -295,17 +314,19 @@ int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out) {
   if (h.magic != kMagic || h.version != kVersion) return QGEMV_ERR_SIZE;
   if (h.total_bytes > bytes) return QGEMV_ERR_SIZE;
   const uint8_t* blob = (const uint8_t*)blob_host;
-  const int chunks = h.K / kChunkCodes, chunk_bytes = 4 * h.bits;
-  uint32_t c[32], dw[4];
-  for (int i = 0; i < h.M; ++i) {
-    const uint8_t* src = blob + h.off_codes + (size_t)i * h.row_bytes;
-    uint8_t* dst = codes_out + (size_t)i * h.K;
-    for (int ch = 0; ch < chunks; ++ch) {
-      std::memcpy(dw, src + (size_t)ch * chunk_bytes, chunk_bytes);
-      unplace_chunk(h.bits, h.format, dw, c);
-      for (int j = 0; j < 32; ++j) dst[ch * 32 + j] = (uint8_t)c[j];
-    }
-  }
+  const int chunk_bytes = 4 * h.bits;
+  uint32_t c[32], dw[4] = {0, 0, 0, 0};
+  for (int t = 0; t < h.tiles; ++t)
+    for (int b = 0; b < h.nkb; ++b)
+      for (int l = 0; l < 64; ++l) {
+        const int row = t * kTileRows + l % 16;
+        if (row >= h.M) continue;
+        std::memcpy(dw, blob + h.off_codes + ((size_t)t * h.nkb + b) * h.block_bytes + (size_t)l * chunk_bytes,
+                    chunk_bytes);
+        unplace_chunk(h.bits, h.format, dw, c);
+        const int k0 = b * kBlockK + 32 * (l / 16);
+        for (int j = 0; j < 32 && k0 + j < h.K; ++j) codes_out[(size_t)row * h.K + k0 + j] = (uint8_t)c[j];
+      }
   return QGEMV_OK;
 }
 

@@ -2,36 +2,42 @@
 //
 // Blob = header | codes | meta | row_ptr | entries, every section 256-byte aligned.
 //
-// codes   M rows of K*bits/8 bytes.  A row is the canonical sequence of 32-code
-//         chunks (chunk c holds canonical codes 32c..32c+31 and occupies the same
-//         4*bits bytes as in the canonical bitstream); only the bit placement
-//         inside a chunk changes, so that each kernel lane turns one dword into
-//         dot-product-ready FP16 pairs with a handful of bitwise ops.  Lane l of
-//         wave step s owns chunk 64*s + l.
+// Tiles.  Rows are grouped in tiles of 16 (the M side of a 16x16x32 MFMA);
+// K is padded to Kp, a multiple of 128, and cut into K-blocks of 128 codes
+// (four MFMA K-steps of 32).  For tile t and K-block b, the 64 lanes of a
+// wave each own one 32-code chunk:
 //
-//         Inside a chunk, pair m (m = 0..15) is canonical codes (2m, 2m+1) and is
-//         multiplied with x[32c + 2m], x[32c + 2m + 1].  Slot placement per format:
+//     lane l  ->  row 16*t + (l % 16),  codes 128*b + 32*(l / 16) .. +31
 //
-//         U4 (uniform, 4 bit; 4 dwords): dword d, slot t = 0..3 holds pair 4d+t;
-//            low code at bits 4t..4t+3, high code at bits 16+4t..16+4t+3.
-//         U3 (uniform, 3 bit; 3 dwords): dword d, slot t = 0..4 holds pair 5d+t;
-//            slots start at bits 0, 3, 6, 10, 13 (low code) and 16 more (high
-//            code).  Pair 15: low code = bit 9 of dwords 0,1,2 (code bits 0,1,2),
-//            high code = bit 25 of dwords 0,1,2.
-//         L4 (LUT, 4 bit; 4 dwords): byte k of dword d holds A = code 8d+k and
-//            B = code 8d+4+k as: bits 0-2 = A&7, bits 3-5 = B&7, bit 6 = A>>3,
-//            bit 7 = B>>3.
-//         L3 (LUT, 3 bit; 3 dwords): byte k of dword d: bits 0-2 = code 8d+k,
-//            bits 3-5 = code 8d+4+k.  Bits 6-7 of the bytes of dword 0 are the
-//            low bits of code 24+k, of dword 1 the low bits of code 28+k; bit 6
-//            (7) of byte k of dword 2 is bit 2 of code 24+k (28+k).
+// which is exactly the A-operand footprint of four 16x16x32 MFMAs (lane l
+// supplies row l % 16 and K-slice 8*(l / 16) .. +7 of each).  The 64 chunks of
+// a (tile, K-block) are stored back to back, lane order, so one wave load of
+// 4*bits bytes per lane reads 768 B (3 bit) or 1 KiB (4 bit) contiguously.
+// Blocks are ordered tile-major: (t, b) at index t * nkb + b.  Padding rows
+// (>= M) and padding columns (>= K) hold code 0 and decode against zero
+// statistics / zero activations.
 //
-// meta    UNIFORM: per row K/16 dwords, dword g = FP16 scale (low half) | FP16
-//         zero (high half) of group g.
-//         LUT: per row the table split into byte planes for v_perm:
-//           3 bit: 4 dwords = lo bytes e0-3, lo e4-7, hi e0-3, hi e4-7
-//           4 bit: 8 dwords = lo e0-3, lo e4-7, lo e8-11, lo e12-15,
-//                             hi e0-3, hi e4-7, hi e8-11, hi e12-15
+// Inside a chunk the 32 codes are re-placed so that a lane turns one dword
+// into FP16 pairs with a few bitwise ops.  Pair m (m = 0..15) is canonical
+// chunk codes (2m, 2m+1); MFMA step i of the K-block takes pairs 4i..4i+3.
+//
+//   U4 (uniform, 4 bit; 4 dwords): dword d, slot t = 0..3 holds pair 4d+t;
+//      low code at bits 4t..4t+3, high code at bits 16+4t..16+4t+3.
+//   U3 (uniform, 3 bit; 3 dwords): dword d, slot t = 0..4 holds pair 5d+t;
+//      slots start at bits 0, 3, 6, 10, 13 (low code) and 16 more (high code).
+//      Pair 15: low code = bit 9 of dwords 0,1,2 (code bits 0,1,2), high code =
+//      bit 25 of dwords 0,1,2.
+//   L4 (LUT, 4 bit; 4 dwords): byte k of dword d holds A = code 8d+k and
+//      B = code 8d+4+k as: bits 0-2 = A&7, bits 3-5 = B&7, bit 6 = A>>3,
+//      bit 7 = B>>3.
+//   L3 (LUT, 3 bit; 3 dwords): byte k of dword d: bits 0-2 = code 8d+k,
+//      bits 3-5 = code 8d+4+k.  Bits 6-7 of the bytes of dword 0 are the low
+//      bits of code 24+k, of dword 1 the low bits of code 28+k; bit 6 (7) of
+//      byte k of dword 2 is bit 2 of code 24+k (28+k).
+//
+// meta    LUT: per row (tiles*16 rows) the canonical FP16 table, 2^bits entries.
+//         UNIFORM: per (tile, K-block, lane) two dwords, one per 16-code group
+//         of the lane's chunk: FP16 scale (low half) | FP16 zero (high half).
 // row_ptr int32 [M+1] (as given).
 // entries uint32 [nnz]: column (low 16 bits) | FP16 value bits (high 16 bits).
 #pragma once
@@ -41,23 +47,24 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 1;
-constexpr int kLanes = 64;
+constexpr uint32_t kVersion = 2;
+constexpr int kTileRows = 16;
+constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
-constexpr int kStepCodes = kLanes * kChunkCodes;  // 2048 codes per wave step
-constexpr int kMaxSteps = 8;                      // K <= 16384
-constexpr int kMaxK = kStepCodes * kMaxSteps;
+constexpr int kMaxK = 16384;
 constexpr uint64_t kAlign = 256;
 constexpr uint64_t kHeaderBytes = 256;
 
 struct BlobHeader {
   uint32_t magic;
   uint32_t version;
-  int32_t M, K, bits, format, group_size, steps;
+  int32_t M, K, bits, format, group_size, tiles;
   int64_t nnz;
   uint64_t off_codes, off_meta, off_rowptr, off_entries, total_bytes;
-  uint32_t row_bytes;       // K * bits / 8
-  uint32_t meta_row_bytes;  // UNIFORM: 4 * K / 16; LUT: 2 << bits
+  uint32_t block_bytes;      // 64 * 4 * bits: codes of one (tile, K-block)
+  uint32_t meta_unit_bytes;  // LUT: bytes per row; UNIFORM: bytes per (tile, K-block)
+  int32_t Kp;                // K padded to a multiple of kBlockK
+  int32_t nkb;               // Kp / kBlockK
 };
 static_assert(sizeof(BlobHeader) <= kHeaderBytes, "header too large");
 
@@ -74,13 +81,18 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
   h.bits = bits;
   h.format = format;
   h.group_size = format == 0 ? group : 0;
-  h.steps = (K + kStepCodes - 1) / kStepCodes;
+  h.tiles = (M + kTileRows - 1) / kTileRows;
   h.nnz = nnz;
-  h.row_bytes = (uint32_t)((int64_t)K * bits / 8);
-  h.meta_row_bytes = format == 0 ? (uint32_t)(4 * (K / group)) : (uint32_t)(2u << bits);
+  h.Kp = (K + kBlockK - 1) / kBlockK * kBlockK;
+  h.nkb = h.Kp / kBlockK;
+  h.block_bytes = (uint32_t)(64 * 4 * bits);
+  h.meta_unit_bytes = format == 0 ? 64u * 8u : (uint32_t)(2u << bits);
+  const uint64_t nblocks = (uint64_t)h.tiles * h.nkb;
+  const uint64_t meta_bytes =
+      format == 0 ? nblocks * h.meta_unit_bytes : (uint64_t)h.tiles * kTileRows * h.meta_unit_bytes;
   h.off_codes = kHeaderBytes;
-  h.off_meta = align_up(h.off_codes + (uint64_t)M * h.row_bytes);
-  h.off_rowptr = align_up(h.off_meta + (uint64_t)M * h.meta_row_bytes);
+  h.off_meta = align_up(h.off_codes + nblocks * h.block_bytes);
+  h.off_rowptr = align_up(h.off_meta + meta_bytes);
   h.off_entries = align_up(h.off_rowptr + 4ull * ((uint64_t)M + 1));
   h.total_bytes = align_up(h.off_entries + 4ull * (uint64_t)nnz);
   return h;
