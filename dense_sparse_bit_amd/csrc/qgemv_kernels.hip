@@ -201,18 +201,23 @@ constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
 // contiguous stretch of the blob -- evenly over its waves.  A wave therefore
 // streams one contiguous run of K-blocks through a ring of PF register slots,
 // crossing a tile boundary at most a few times; at each crossing it parks its
-// partial sums for the finished tile in LDS.  After the stream each wave sums
-// the outliers of its rows, and after one barrier the partials of every tile
-// are added in a fixed order: two barriers per launch, deterministic output.
+// partial sums for the finished tile in LDS.
+//
+// The outliers of the workgroup's rows are one contiguous run of CSR entries.
+// Right after the prologue the waves copy that run (up to the LDS space left)
+// from HBM straight into LDS with buffer-to-LDS loads, which complete in the
+// background while the dense stream runs.  After the stream each wave sums
+// the outliers of its rows from LDS, and the partials of every row are added
+// in a fixed order: the output is deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 16;
-constexpr int kCsrRows = 8;  // outlier rows per wave whose first entries are prefetched
+constexpr uint32_t kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), no wait on the other counters
 
-template <int FMT, int BITS, int PF, int NE>
+template <int FMT, int BITS, int PF>
 __global__ void __launch_bounds__(64 * kWaves)
 k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
      const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
-     int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz) {
+     int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap) {
   using F = Fmt<FMT, BITS>;
   constexpr int BB = 256 * BITS;
   extern __shared__ uint32_t lds[];
@@ -228,17 +233,20 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
   // LDS: x [Kp] fp16 | partials [TW][kWaves][16] | csr [TW*16] | row_ptr [TW*16+4] | LUT [TW*16][tab_dw]
+  //      | CSR entries [ent_cap]
   uint16_t* x_lds = (uint16_t*)lds;
   float* part = (float*)(lds + Kp / 2);
   float* csr = part + TW * kWaves * 16;
   int* rp_lds = (int*)(csr + TW * 16);
   uint32_t* lut_lds = (uint32_t*)(rp_lds + TW * 16 + 4);  // 16-byte aligned
+  uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);
 
   const rsrc_t rc = make_rsrc(codes, codes_bytes);
   const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
+  const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
 
-  // The code ring goes out first; x, the row_ptr slice and the tables follow
-  // and land in LDS while the ring is in flight.
+  // Prologue: the code ring, then x, the row_ptr slice and the tables; all of
+  // them are in flight together.
   const uint32_t voff = (uint32_t)lane * 4 * BITS;
   const uint32_t soff = (uint32_t)lane * 8;
   uint32_t cb[PF][BITS];
@@ -250,6 +258,8 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
     if constexpr (!F::lut) load_stats(sb[u], rs, g < g1 ? (uint32_t)g * 512 + soff : kOutOfRange);
     else sb[u][0] = sb[u][1] = 0;
   }
+  const int E0 = row_ptr[T0 * 16];            // outliers of the workgroup: entries [E0, E1)
+  const int E1 = row_ptr[T0 * 16 + nrows];
   {
     const rsrc_t rx = make_rsrc(x, (uint32_t)K * 2);
     for (int i = threadIdx.x; i < Kp / 8; i += 64 * kWaves)
@@ -267,18 +277,18 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
   }
   __syncthreads();
 
-  // First NE*64 entries of each of this wave's outlier rows (rows w, w+16, ...).
-  const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
-  uint32_t ent[kCsrRows][NE];
-#pragma unroll
-  for (int j = 0; j < kCsrRows; ++j) {
-    const int r = w + 16 * j;
-    const int p0 = r < nrows ? rp_lds[r] : 0;
-    const int cnt = r < nrows ? rp_lds[r + 1] - p0 : 0;
-#pragma unroll
-    for (int k = 0; k < NE; ++k) {
-      const int q = lane + 64 * k;
-      ent[j][k] = __builtin_amdgcn_raw_buffer_load_b32(re, q < cnt ? (p0 + q) * 4 : (int)kOutOfRange, 0, 0);
+  // CSR entries [A0, A0 + ent_cap) of the workgroup's run go to LDS, 1 KiB per
+  // wave instruction (16 bytes per lane); issued after the barrier so that
+  // nothing waits on them before the stream ends.
+  const int A0 = E0 & ~3;
+  const int Acap = min(E1, A0 + ent_cap);
+  {
+    const int pieces = (Acap - A0 + 3) >> 2;
+    for (int i = w; 64 * i < pieces; i += kWaves) {
+      const int piece = 64 * i + lane;
+      if (piece < pieces)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(ent_lds + 256 * i), 16,
+                                                 (A0 + 4 * piece) * 4, 0, 0, 0);
     }
   }
 
@@ -338,37 +348,15 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
   }
   if (g1 > g0) flush();
 
-  // Outliers of this wave's rows; entries past the prefetched ones are read
-  // four wave-loads at a time.
-  for (int j = 0; w + 16 * j < nrows; ++j) {
-    const int r = w + 16 * j;
-    const int p0 = rp_lds[r];
-    const int cnt = rp_lds[r + 1] - p0;
+  // Outliers: entries of the LDS run come from LDS, any beyond it from HBM.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  for (int r = w; r < nrows; r += kWaves) {
+    const int p1 = rp_lds[r + 1];
     float sum = 0.f;
-    int k0 = 0;
-    if (j < kCsrRows) {
-#pragma unroll
-      for (int jj = 0; jj < kCsrRows; ++jj)
-        if (jj == j) {
-#pragma unroll
-          for (int k = 0; k < NE; ++k)
-            if (lane + 64 * k < cnt) {
-              const uint32_t e = ent[jj][k];
-              sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
-            }
-        }
-      k0 = NE;
-    }
-    for (int k = k0; 64 * k < cnt; k += 4) {
-      uint32_t e4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = lane + 64 * (k + i);
-        e4[i] = __builtin_amdgcn_raw_buffer_load_b32(re, q < cnt ? (p0 + q) * 4 : (int)kOutOfRange, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * (k + i) < cnt) sum = dot2(e4[i] >> 16, (uint32_t)x_lds[e4[i] & 0xFFFFu], sum);
+    for (int p = rp_lds[r] + lane; p < p1; p += 64) {
+      const uint32_t e = p < Acap ? ent_lds[p - A0] : entries[p];
+      sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
     }
     sum = wave_sum(sum);
     if (lane == 0) csr[r] = sum;
@@ -380,6 +368,159 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) v += pr[ww * 16];
     y[T0 * 16 + r] = v + csr[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Batch 8 / 16.  The dequantized tile is the A operand and the activations
+// are the B operand of the same 16x16x32 MFMA: column n of the product is
+// batch row n, so one MFMA serves the whole batch (columns n >= batch read
+// zeros).  One workgroup owns one tile; its waves split the tile's K-blocks.
+// x is 4 KiB per K-block at batch 16 and comes from L2 through the register
+// ring, next to the codes of the same K-block.  The dense kernel writes y;
+// the outliers are added by k_csr_bn on the same stream.
+// ---------------------------------------------------------------------------
+template <int FMT, int BITS, int PF>
+__global__ void __launch_bounds__(64 * kWaves)
+k_bn(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const uint16_t* __restrict__ x,
+     float* __restrict__ y, int M, int K, int nkb, uint32_t codes_bytes, uint32_t meta_bytes, int B) {
+  using F = Fmt<FMT, BITS>;
+  constexpr int BB = 256 * BITS;
+  __shared__ float part[kWaves][256];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int t = blockIdx.x;
+  const int b0 = w * nkb / nw, b1 = (w + 1) * nkb / nw;  // this wave's K-blocks of tile t
+  const int g0 = t * nkb + b0, g1 = t * nkb + b1;
+
+  const rsrc_t rc = make_rsrc(codes, codes_bytes);
+  const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)B * (uint32_t)K * 2u);
+  const uint32_t voff = (uint32_t)lane * 4 * BITS;
+  const uint32_t soff = (uint32_t)lane * 8;
+  const int n = lane & 15;
+  // B operand of lane (n, q = lane / 16) for K-block kb: x[n][128 kb + 32 q .. +31], 64 bytes.
+  const uint32_t xrow = n < B ? (uint32_t)n * (uint32_t)K * 2u + 64u * (uint32_t)(lane >> 4) : kOutOfRange;
+  auto xoff = [&](int kb) -> uint32_t {
+    return (xrow != kOutOfRange && 128 * kb + 32 * (lane >> 4) < K) ? xrow + 256u * (uint32_t)kb : kOutOfRange;
+  };
+
+  uint32_t cb[PF][BITS];
+  uint32_t sb[PF][2];
+  u32x4_t xr[PF][4];
+  auto issue = [&](int u, int g) {
+    const bool in = g < g1;
+    load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
+    if constexpr (!F::lut) load_stats(sb[u], rs, in ? (uint32_t)g * 512 + soff : kOutOfRange);
+    const uint32_t xo = in ? xoff(g - t * nkb) : kOutOfRange;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      xr[u][s2] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo == kOutOfRange ? kOutOfRange : xo + 16u * s2), 0, 0);
+  };
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    if constexpr (F::lut) sb[u][0] = sb[u][1] = 0;
+    issue(u, g0 + u);
+  }
+  uint32_t tab[F::tab_dw];
+  if constexpr (F::lut) {
+    const rsrc_t rl = make_rsrc(meta, meta_bytes);
+    const uint32_t off = ((uint32_t)t * 16 + (lane & 15)) * (F::tab_dw * 4);
+    uint32_t L[F::tab_dw];
+    const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(rl, (int)off, 0, 0);
+    L[0] = v0[0]; L[1] = v0[1]; L[2] = v0[2]; L[3] = v0[3];
+    if constexpr (BITS == 4) {
+      const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(rl, (int)(off + 16), 0, 0);
+      L[4] = v1[0]; L[5] = v1[1]; L[6] = v1[2]; L[7] = v1[3];
+      l4_planes(L, tab);
+    } else {
+      l3_planes(L, tab);
+    }
+  } else {
+    tab[0] = 0;
+  }
+
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int gi = g0; gi < g1; gi += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int g = gi + u;
+      if (g < g1) {
+        uint32_t am[F::n_mfma][4];
+        decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const half8_t bx = __builtin_bit_cast(half8_t, xr[u][s2]);
+          acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
+          if constexpr (!F::lut) acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+        }
+      }
+      issue(u, g + PF);
+    }
+  }
+  // acc: row 4*(lane/16) + r, batch column lane % 16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[w][(4 * (lane >> 4) + r) * 16 + n] = acc[r];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    const int m = i >> 4, c = i & 15, row = 16 * t + m;
+    if (c < B && row < M) {
+      float v = 0.f;
+      for (int ww = 0; ww < nw; ++ww) v += part[ww][i];
+      y[(size_t)c * M + row] = v;
+    }
+  }
+}
+
+// Outliers at batch 8 / 16: y[n][r] += sum_p value_p * x[n][col_p].  A
+// workgroup owns a run of rows.  x is staged transposed in LDS, KC columns at
+// a time, so one entry meets all batch rows in one place; lane (n, slot) of a
+// wave takes batch row n of entry slot.  Every y element is updated by exactly
+// one lane, after the dense kernel on the same stream: no atomics, fixed order.
+template <int NB>
+__global__ void __launch_bounds__(256)
+k_csr_bn(const int32_t* __restrict__ row_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x,
+         float* __restrict__ y, int M, int K, int B, int rows_per_wg, int KC) {
+  constexpr int SL = 64 / NB;           // entry slots per wave instruction
+  constexpr int kRowsPerWave = 8;
+  extern __shared__ uint16_t xT[];      // [KC][NB]
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane % NB, sl = lane / NB;
+  const int R0 = blockIdx.x * rows_per_wg;
+  const int R1 = min(M, R0 + rows_per_wg);
+  float acc[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) acc[j] = 0.f;
+  for (int c0 = 0; c0 < K; c0 += KC) {
+    const int kc = min(KC, K - c0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kc * NB; i += blockDim.x) {
+      const int nn = i / kc, k = i - nn * kc;  // read x row-wise, write transposed
+      xT[k * NB + nn] = nn < B ? x[(size_t)nn * K + c0 + k] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int r = R0 + w + 4 * j;
+      if (r < R1) {
+        const int p1 = row_ptr[r + 1];
+        for (int p = row_ptr[r] + sl; p < p1; p += SL) {
+          const uint32_t e = entries[p];
+          const int col = (int)(e & 0xFFFFu) - c0;
+          if (col >= 0 && col < kc) acc[j] = dot2(e >> 16, (uint32_t)xT[col * NB + n], acc[j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    float v = acc[j];
+    for (int o = NB; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    const int r = R0 + w + 4 * j;
+    if (sl == 0 && r < R1 && n < B) y[(size_t)n * M + r] += v;
   }
 }
 
@@ -469,7 +610,12 @@ int b1_grid(const BlobHeader& h) {
   return g > need ? g : need;
 }
 
-size_t b1_lds_bytes(const BlobHeader& h, int grid) {
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr size_t kEntCapBytes = 64 * 1024;  // CSR entries staged per workgroup
+constexpr size_t kCsrStageBytes = 64 * 1024;  // transposed x per staging pass of k_csr_bn
+
+// LDS of everything but the staged CSR entries.
+size_t b1_lds_fixed(const BlobHeader& h, int grid) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
   const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
   return (size_t)h.Kp * 2 + tw * kWaves * 16 * 4 + tw * 16 * 4 + (tw * 16 + 4) * 4 + tw * 16 * tab;
@@ -477,23 +623,52 @@ size_t b1_lds_bytes(const BlobHeader& h, int grid) {
 
 template <int FMT, int BITS>
 hipError_t launch_b1(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int PF = 8, NE = 2;
+  constexpr int PF = 8;
   const BlobHeader& h = p->h;
   const int grid = b1_grid(h);
-  const size_t lds = b1_lds_bytes(h, grid);
+  const size_t fixed = b1_lds_fixed(h, grid);
+  size_t cap = kLdsBytes - fixed;
+  if (cap > kEntCapBytes) cap = kEntCapBytes;
+  cap &= ~(size_t)1023;  // whole 1 KiB wave loads
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_b1<FMT, BITS, PF, NE>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    const hipError_t e = hipFuncSetAttribute((const void*)k_b1<FMT, BITS, PF>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
-  hipLaunchKernelGGL((k_b1<FMT, BITS, PF, NE>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
+  hipLaunchKernelGGL((k_b1<FMT, BITS, PF>), dim3(grid), dim3(64 * kWaves), fixed + cap, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
                      (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
-                     meta_bytes, (int)h.nnz);
+                     meta_bytes, (int)h.nnz, (int)(cap / 4));
+  return hipGetLastError();
+}
+
+template <int FMT, int BITS>
+hipError_t launch_bn(const qgemv_plan* p, const uint16_t* x, float* y, int B, hipStream_t st) {
+  constexpr int PF = 3;
+  const BlobHeader& h = p->h;
+  int waves = h.nkb / 4;  // at least 4 K-blocks per wave
+  waves = waves < 1 ? 1 : (waves > kWaves ? kWaves : waves);
+  const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
+  const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
+  hipLaunchKernelGGL((k_bn<FMT, BITS, PF>), dim3(h.tiles), dim3(64 * waves), 0, st, p->blob + h.off_codes,
+                     (const uint32_t*)(p->blob + h.off_meta), x, y, h.M, h.K, h.nkb, codes_bytes, meta_bytes, B);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || h.nnz == 0) return e;
+  const int rows_per_wg = 4 * 8;  // 4 waves x 8 rows
+  const int grid = (h.M + rows_per_wg - 1) / rows_per_wg;
+  const int nb = B <= 8 ? 8 : 16;
+  const int KC = (int)(kCsrStageBytes / (2 * nb));
+  const size_t lds = (size_t)(KC < h.K ? KC : h.K) * nb * 2;
+  const int32_t* rp = (const int32_t*)(p->blob + h.off_rowptr);
+  const uint32_t* ent = (const uint32_t*)(p->blob + h.off_entries);
+  if (nb == 8)
+    hipLaunchKernelGGL((k_csr_bn<8>), dim3(grid), dim3(256), lds, st, rp, ent, x, y, h.M, h.K, B, rows_per_wg, KC);
+  else
+    hipLaunchKernelGGL((k_csr_bn<16>), dim3(grid), dim3(256), lds, st, rp, ent, x, y, h.M, h.K, B, rows_per_wg, KC);
   return hipGetLastError();
 }
 
@@ -540,15 +715,20 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
   if (!h || !x_dev || !y_dev) return QGEMV_ERR_INVALID_ARG;
   if ((uintptr_t)x_dev % 16 || (uintptr_t)y_dev % 16) return QGEMV_ERR_INVALID_ARG;
   if (batch != 1 && batch != 8 && batch != 16) return QGEMV_ERR_UNSUPPORTED;
-  if (batch != 1) return QGEMV_ERR_UNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   const uint16_t* x = (const uint16_t*)x_dev;
+  const bool lut = h->h.format == QGEMV_FMT_LUT, b4 = h->h.bits == 4;
   hipError_t e;
-  if (h->h.format == QGEMV_FMT_LUT)
-    e = h->h.bits == 4 ? launch_b1<QGEMV_FMT_LUT, 4>(h, x, y_dev, st) : launch_b1<QGEMV_FMT_LUT, 3>(h, x, y_dev, st);
-  else
-    e = h->h.bits == 4 ? launch_b1<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, st)
-                       : launch_b1<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, st);
+  if (batch == 1) {
+    if (lut) e = b4 ? launch_b1<QGEMV_FMT_LUT, 4>(h, x, y_dev, st) : launch_b1<QGEMV_FMT_LUT, 3>(h, x, y_dev, st);
+    else e = b4 ? launch_b1<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, st) : launch_b1<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, st);
+  } else {
+    if (lut)
+      e = b4 ? launch_bn<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_bn<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
+    else
+      e = b4 ? launch_bn<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, batch, st)
+             : launch_bn<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, batch, st);
+  }
   return hip_status(e);
 }
 

@@ -69,8 +69,17 @@ def run_b1(torch, plan, x16, canary=True):
     return y.cpu().numpy().astype(np.float64)
 
 
+def run_bn(torch, plan, x16):
+    """Batched run (B = rows of x16) into a NaN-filled y."""
+    x = torch.from_numpy(np.ascontiguousarray(x16)).cuda()
+    y = torch.full((x16.shape[0], plan.M), float("nan"), dtype=torch.float32, device="cuda")
+    y = plan.run(x, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
 def check_y(y_gpu, enc, x16, rows=None):
-    y_ref, A = gemv.gemv_rows(enc, x16[:1], rows)
+    y_ref, A = gemv.gemv_rows(enc, x16[:y_gpu.shape[0]], rows)
     yg = y_gpu if rows is None else y_gpu[:, rows]
     assert np.all(np.isfinite(yg)), "output not fully written"
     ok, worst = gemv.within_tolerance(yg, y_ref, A)
@@ -211,3 +220,80 @@ def test_side_stream(torch):
         y = plan.run(x)
     st.synchronize()
     check_y(y.cpu().numpy().astype(np.float64), enc, x16)
+
+
+# ---- batch 8 / 16 (MFMA path) ------------------------------------------------
+
+BATCHED_SMALL = [
+    ("tiny_u4", None, None, 16),
+    ("attn7b_u3", 200, 2080, 16),
+    ("mlp7b_lut3", 33, 4128, 8),
+    ("mlp70b_lut4", 24, 8192, 8),
+    ("mlp70b_lut4", 40, 2080, 16),
+    ("block7b_u3", 96, 11008, 16),
+]
+
+
+@pytest.mark.parametrize("name,M,K,B", BATCHED_SMALL)
+def test_batched_oracle_encoded(torch, name, M, K, B):
+    enc, _ = oracle_case(name, M, K)
+    wl = WORKLOADS[name]
+    x16 = make_x(wl, B, enc["K"], 0, enc["M"])
+    _say(f"[gpu] batched {name} B={B} M={enc['M']} K={enc['K']} nnz={enc['row_ptr'][-1]}")
+    plan = qgemv.QGemv(enc)
+    y1 = run_bn(torch, plan, x16)
+    check_y(y1, enc, x16)
+    y2 = run_bn(torch, plan, x16)
+    assert np.array_equal(y1, y2), "not bitwise deterministic"
+    plan.close()
+
+
+@pytest.mark.parametrize("name,layer,B", [("mlp70b_lut4", 0, 8), ("block7b_u3", 0, 16), ("block7b_u3", 4, 16),
+                                          ("block7b_u3", 6, 16)])
+def test_batched_full_size_sampled(torch, name, layer, B):
+    f = format_case(name, layer)
+    M, K = f["M"], f["K"]
+    _say(f"[gpu] batched full {name} layer={layer} B={B} M={M} K={K} nnz={f['row_ptr'][-1]}")
+    x16 = make_x(name, B, K, layer, M)
+    plan = qgemv.QGemv(f)
+    y = run_bn(torch, plan, x16)
+    assert np.all(np.isfinite(y)), "output not fully written"
+    rng = np.random.default_rng(321)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, 256), replace=False)]))
+    check_y(y, f, x16, rows)
+    heavy = np.argsort(-np.diff(f["row_ptr"]), kind="stable")[:16]
+    check_y(y, f, x16, np.sort(heavy))
+    plan.close()
+
+
+@pytest.mark.parametrize("fmt,bits", [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4)])
+@pytest.mark.parametrize("B", [8, 16])
+def test_batched_edge_cases(torch, fmt, bits, B):
+    cases = {
+        "no_outliers": _custom(fmt, bits, 70, 2048, [0] * 70, seed=1),
+        "single_row": _custom(fmt, bits, 1, 4096, [5], seed=2),
+        "k32": _custom(fmt, bits, 300, 32, [1] * 300, seed=3),
+        "dense_csr_rows": _custom(fmt, bits, 9, 4096, [0, 700, 64, 65, 128, 320, 321, 1, 4096], seed=4),
+        "max_k": _custom(fmt, bits, 5, 16384, [3, 0, 500, 7, 16384], seed=5),
+    }
+    for label, f in cases.items():
+        _say(f"[gpu] batched edge {fmt}{bits} B={B} {label} M={f['M']} K={f['K']} nnz={f['row_ptr'][-1]}")
+        x16 = np.random.default_rng(9).standard_normal((B, f["K"])).astype(np.float16)
+        plan = qgemv.QGemv(f)
+        y = run_bn(torch, plan, x16)
+        check_y(y, f, x16)
+        plan.close()
+
+
+def test_batched_rows_match_single(torch):
+    """Each batch row of a batched run meets the tolerance of, and stays close to, its own batch-1 run."""
+    enc, _ = oracle_case("mlp70b_lut4", 40, 2080)
+    x16 = make_x(WORKLOADS["mlp70b_lut4"], 8, enc["K"], 0, enc["M"])
+    plan = qgemv.QGemv(enc)
+    yb = run_bn(torch, plan, x16)
+    for b in range(8):
+        y1 = run_b1(torch, plan, x16[b:b + 1])
+        check_y(y1, enc, x16[b:b + 1])
+        _, A = gemv.gemv_rows(enc, x16[b:b + 1])
+        assert np.all(np.abs(yb[b] - y1[0]) <= 2e-4 * A[0] + 2e-6)
+    plan.close()
