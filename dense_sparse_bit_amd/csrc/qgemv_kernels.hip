@@ -196,30 +196,40 @@ __device__ __forceinline__ void load_stats(uint32_t (&s)[2], rsrc_t r, uint32_t 
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
 
 // ---------------------------------------------------------------------------
-// Batch 1.  One workgroup of 16 waves per CU owns the contiguous tile range
-// [T0, T1) and splits its (tile, K-block) pairs -- tile-major, i.e. one
-// contiguous stretch of the blob -- evenly over its waves.  A wave therefore
-// streams one contiguous run of K-blocks through a ring of PF register slots,
-// crossing a tile boundary at most a few times; at each crossing it parks its
-// partial sums for the finished tile in LDS.
+// The streaming kernel.  One workgroup of 16 waves per CU owns the contiguous
+// tile range [T0, T1) and splits its (tile, K-block) pairs -- tile-major, i.e.
+// one contiguous stretch of the blob -- evenly over its waves.  A wave
+// therefore streams one contiguous run of K-blocks through a ring of PF
+// register slots, crossing a tile boundary at most a few times; at each
+// crossing it parks its partial sums for the finished tile in LDS.  After the
+// stream the partials of every output are added in a fixed order, so the
+// output is deterministic.
 //
-// The outliers of the workgroup's rows are one contiguous run of CSR entries.
-// Right after the prologue the waves copy that run (up to the LDS space left)
-// from HBM straight into LDS with buffer-to-LDS loads, which complete in the
-// background while the dense stream runs.  After the stream each wave sums
-// the outliers of its rows from LDS, and the partials of every row are added
-// in a fixed order: the output is deterministic.
+// Batch 1 (NB = 1): x sits in LDS and every lane reads its B operand from
+// there (the same x in all 16 MFMA columns).  The outliers of the
+// workgroup's rows are one contiguous run of CSR entries; right after the
+// prologue barrier the waves copy that run (up to the LDS space left) from HBM
+// straight into LDS with buffer-to-LDS loads, which land while the dense
+// stream runs.  After the stream each wave sums the outliers of its rows from
+// LDS.
+//
+// Batch 8 / 16 (NB = batch): column n of the MFMA is batch row n.  x is
+// 2 KiB or 4 KiB per K-block and comes from L2 through the ring, next to the
+// codes of the same K-block; partials are kept per batch column.  The CSR run
+// is staged in LDS the same way; after the stream x is staged transposed in
+// LDS, KC columns per pass, and each outlier meets all batch rows at once.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 16;
 constexpr uint32_t kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), no wait on the other counters
 
-template <int FMT, int BITS, int PF>
+template <int FMT, int BITS, int PF, int NB>
 __global__ void __launch_bounds__(64 * kWaves)
-k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
-     const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
-     int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap) {
+k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
+         const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
+         int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap, int KC) {
   using F = Fmt<FMT, BITS>;
   constexpr int BB = 256 * BITS;
+  constexpr bool B1 = NB == 1;
   extern __shared__ uint32_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -232,57 +242,78 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
   const int g1 = T0 * nkb + (w + 1) * nblk / kWaves;
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
-  // LDS: x [Kp] fp16 | partials [TW][kWaves][16] | csr [TW*16] | row_ptr [TW*16+4] | LUT [TW*16][tab_dw]
-  //      | CSR entries [ent_cap]
+  // LDS: x [Kp] fp16 (batch 1 only) | part [TW][kWaves][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+4]
+  //      | LUT [TW*16][tab_dw] | CSR entries [ent_cap] | x transposed [KC+1][NB/2] FP16 pairs (batch NB only)
   uint16_t* x_lds = (uint16_t*)lds;
-  float* part = (float*)(lds + Kp / 2);
-  float* csr = part + TW * kWaves * 16;
-  int* rp_lds = (int*)(csr + TW * 16);
+  float* part = (float*)(lds + (B1 ? Kp / 2 : 0));
+  float* csr = part + TW * kWaves * 16 * NB;
+  int* rp_lds = (int*)(csr + TW * 16 * NB);
   uint32_t* lut_lds = (uint32_t*)(rp_lds + TW * 16 + 4);  // 16-byte aligned
   uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);
+  uint32_t* xT = ent_lds + ent_cap;
 
   const rsrc_t rc = make_rsrc(codes, codes_bytes);
   const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
-  const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)NB * (uint32_t)K * 2u);
 
-  // Prologue: the code ring, then x, the row_ptr slice and the tables; all of
-  // them are in flight together.
+  // B operand of lane (n, q) = (lane % 16, lane / 16) for K-block kb, batch NB:
+  // x[n][128 kb + 32 q .. +31], 64 bytes.
+  const uint32_t xrow = (lane & 15) < NB ? (uint32_t)(lane & 15) * (uint32_t)K * 2u + 64u * (uint32_t)(lane >> 4)
+                                         : kOutOfRange;
+  const int xq = 32 * (lane >> 4);
+
+  // Prologue: the ring first, then what goes to LDS; all of it is in flight together.
   const uint32_t voff = (uint32_t)lane * 4 * BITS;
   const uint32_t soff = (uint32_t)lane * 8;
   uint32_t cb[PF][BITS];
   uint32_t sb[PF][2];
-#pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    const int g = g0 + u;
-    load_chunk<BITS>(cb[u], rc, g < g1 ? (uint32_t)g * BB + voff : kOutOfRange);
-    if constexpr (!F::lut) load_stats(sb[u], rs, g < g1 ? (uint32_t)g * 512 + soff : kOutOfRange);
+  u32x4_t xr[B1 ? 1 : PF][4];
+  int ikb = g0 % nkb;  // K-block index of the next block to issue
+  auto issue = [&](int u, int g) {
+    const bool in = g < g1;
+    load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
+    if constexpr (!F::lut) load_stats(sb[u], rs, in ? (uint32_t)g * 512 + soff : kOutOfRange);
     else sb[u][0] = sb[u][1] = 0;
-  }
-  const int E0 = row_ptr[T0 * 16];            // outliers of the workgroup: entries [E0, E1)
+    if constexpr (!B1) {
+      const uint32_t xo = in && xrow != kOutOfRange && 128 * ikb + xq < K ? xrow + 256u * (uint32_t)ikb : kOutOfRange;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        xr[u][s2] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo == kOutOfRange ? kOutOfRange : xo + 16u * s2),
+                                                          0, 0);
+      ikb = ikb + 1 == nkb ? 0 : ikb + 1;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < PF; ++u) issue(u, g0 + u);
+
+  const int E0 = row_ptr[T0 * 16];  // outliers of the workgroup: entries [E0, E1)
   const int E1 = row_ptr[T0 * 16 + nrows];
-  {
-    const rsrc_t rx = make_rsrc(x, (uint32_t)K * 2);
+  if constexpr (B1) {
     for (int i = threadIdx.x; i < Kp / 8; i += 64 * kWaves)
       ((u32x4_t*)x_lds)[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, i * 16, 0, 0);
+  }
+  {
     const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
     for (int i = threadIdx.x; i <= TW * 16; i += 64 * kWaves)
       rp_lds[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, min(T0 * 16 + i, M) * 4, 0, 0);
-    if constexpr (F::lut) {
-      const rsrc_t rl = make_rsrc(meta, meta_bytes);
-      const int n = TW * 16 * F::tab_dw / 4;  // 16-byte pieces
-      for (int i = threadIdx.x; i < n; i += 64 * kWaves)
-        ((u32x4_t*)lut_lds)[i] = __builtin_amdgcn_raw_buffer_load_b128(rl, (T0 * 16 * F::tab_dw / 4 + i) * 16, 0, 0);
-    }
-    for (int j = lane; j < TW * 16; j += 64) part[((j >> 4) * kWaves + w) * 16 + (j & 15)] = 0.f;
   }
+  if constexpr (F::lut) {
+    const rsrc_t rl = make_rsrc(meta, meta_bytes);
+    const int n = TW * 16 * F::tab_dw / 4;  // 16-byte pieces
+    for (int i = threadIdx.x; i < n; i += 64 * kWaves)
+      ((u32x4_t*)lut_lds)[i] = __builtin_amdgcn_raw_buffer_load_b128(rl, (T0 * 16 * F::tab_dw / 4 + i) * 16, 0, 0);
+  }
+  for (int j = lane; j < TW * 16 * NB; j += 64)
+    part[((j / (16 * NB)) * kWaves + w) * 16 * NB + j % (16 * NB)] = 0.f;
   __syncthreads();
 
-  // CSR entries [A0, A0 + ent_cap) of the workgroup's run go to LDS, 1 KiB per
-  // wave instruction (16 bytes per lane); issued after the barrier so that
+  // CSR entries [A0, A0 + ent_cap) of the workgroup's run go to LDS, 1 KiB
+  // per wave instruction (16 bytes per lane); issued after the barrier so that
   // nothing waits on them before the stream ends.
   const int A0 = E0 & ~3;
   const int Acap = min(E1, A0 + ent_cap);
   {
+    const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
     const int pieces = (Acap - A0 + 3) >> 2;
     for (int i = w; 64 * i < pieces; i += kWaves) {
       const int piece = 64 * i + lane;
@@ -309,13 +340,18 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
   };
   planes();
 
-  const uint16_t* xb = x_lds + 32 * (lane >> 4);
+  const uint16_t* xb = x_lds + xq;
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto flush = [&]() {  // rows 4*(lane/16) .. +3 of the tile sit in lanes 0, 16, 32, 48
-    if ((lane & 15) == 0) {
-      float* sl = part + ((tc - T0) * kWaves + w) * 16 + 4 * (lane >> 4);
+  auto flush = [&]() {  // acc[r]: row 4*(lane/16) + r of the tile, batch column lane % 16
+    float* sl = part + ((tc - T0) * kWaves + w) * 16 * NB;
+    if constexpr (B1) {
+      if ((lane & 15) == 0)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sl[r] = acc[r];
+        for (int r = 0; r < 4; ++r) sl[4 * (lane >> 4) + r] = acc[r];
+    } else {
+      if ((lane & 15) < NB)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl[(4 * (lane >> 4) + r) * NB + (lane & 15)] = acc[r];
     }
     acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   };
@@ -332,18 +368,17 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
         }
         uint32_t am[F::n_mfma][4];
         decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
-        const uint16_t* xk = xb + kb * kBlockK;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          const half8_t bx = *(const half8_t*)(xk + 8 * s2);
+          half8_t bx;
+          if constexpr (B1) bx = *(const half8_t*)(xb + kb * kBlockK + 8 * s2);
+          else bx = __builtin_bit_cast(half8_t, xr[u][s2]);
           acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
           if constexpr (!F::lut) acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
         }
         ++kb;
       }
-      const int gn = g + PF;
-      load_chunk<BITS>(cb[u], rc, gn < g1 ? (uint32_t)gn * BB + voff : kOutOfRange);
-      if constexpr (!F::lut) load_stats(sb[u], rs, gn < g1 ? (uint32_t)gn * 512 + soff : kOutOfRange);
+      issue(u, g + PF);
     }
   }
   if (g1 > g0) flush();
@@ -351,176 +386,111 @@ k_b1(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const
   // Outliers: entries of the LDS run come from LDS, any beyond it from HBM.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
-  for (int r = w; r < nrows; r += kWaves) {
-    const int p1 = rp_lds[r + 1];
-    float sum = 0.f;
-    for (int p = rp_lds[r] + lane; p < p1; p += 64) {
-      const uint32_t e = p < Acap ? ent_lds[p - A0] : entries[p];
-      sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) csr[r] = sum;
-  }
-  __syncthreads();
-  for (int r = threadIdx.x; r < nrows; r += 64 * kWaves) {
-    const float* pr = part + (r >> 4) * kWaves * 16 + (r & 15);
-    float v = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) v += pr[ww * 16];
-    y[T0 * 16 + r] = v + csr[r];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Batch 8 / 16.  The dequantized tile is the A operand and the activations
-// are the B operand of the same 16x16x32 MFMA: column n of the product is
-// batch row n, so one MFMA serves the whole batch (columns n >= batch read
-// zeros).  One workgroup owns one tile; its waves split the tile's K-blocks.
-// x is 4 KiB per K-block at batch 16 and comes from L2 through the register
-// ring, next to the codes of the same K-block.  The dense kernel writes y;
-// the outliers are added by k_csr_bn on the same stream.
-// ---------------------------------------------------------------------------
-template <int FMT, int BITS, int PF>
-__global__ void __launch_bounds__(64 * kWaves)
-k_bn(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const uint16_t* __restrict__ x,
-     float* __restrict__ y, int M, int K, int nkb, uint32_t codes_bytes, uint32_t meta_bytes, int B) {
-  using F = Fmt<FMT, BITS>;
-  constexpr int BB = 256 * BITS;
-  __shared__ float part[kWaves][256];
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
-  const int t = blockIdx.x;
-  const int b0 = w * nkb / nw, b1 = (w + 1) * nkb / nw;  // this wave's K-blocks of tile t
-  const int g0 = t * nkb + b0, g1 = t * nkb + b1;
-
-  const rsrc_t rc = make_rsrc(codes, codes_bytes);
-  const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
-  const rsrc_t rx = make_rsrc(x, (uint32_t)B * (uint32_t)K * 2u);
-  const uint32_t voff = (uint32_t)lane * 4 * BITS;
-  const uint32_t soff = (uint32_t)lane * 8;
-  const int n = lane & 15;
-  // B operand of lane (n, q = lane / 16) for K-block kb: x[n][128 kb + 32 q .. +31], 64 bytes.
-  const uint32_t xrow = n < B ? (uint32_t)n * (uint32_t)K * 2u + 64u * (uint32_t)(lane >> 4) : kOutOfRange;
-  auto xoff = [&](int kb) -> uint32_t {
-    return (xrow != kOutOfRange && 128 * kb + 32 * (lane >> 4) < K) ? xrow + 256u * (uint32_t)kb : kOutOfRange;
-  };
-
-  uint32_t cb[PF][BITS];
-  uint32_t sb[PF][2];
-  u32x4_t xr[PF][4];
-  auto issue = [&](int u, int g) {
-    const bool in = g < g1;
-    load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
-    if constexpr (!F::lut) load_stats(sb[u], rs, in ? (uint32_t)g * 512 + soff : kOutOfRange);
-    const uint32_t xo = in ? xoff(g - t * nkb) : kOutOfRange;
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      xr[u][s2] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo == kOutOfRange ? kOutOfRange : xo + 16u * s2), 0, 0);
-  };
-#pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    if constexpr (F::lut) sb[u][0] = sb[u][1] = 0;
-    issue(u, g0 + u);
-  }
-  uint32_t tab[F::tab_dw];
-  if constexpr (F::lut) {
-    const rsrc_t rl = make_rsrc(meta, meta_bytes);
-    const uint32_t off = ((uint32_t)t * 16 + (lane & 15)) * (F::tab_dw * 4);
-    uint32_t L[F::tab_dw];
-    const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(rl, (int)off, 0, 0);
-    L[0] = v0[0]; L[1] = v0[1]; L[2] = v0[2]; L[3] = v0[3];
-    if constexpr (BITS == 4) {
-      const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(rl, (int)(off + 16), 0, 0);
-      L[4] = v1[0]; L[5] = v1[1]; L[6] = v1[2]; L[7] = v1[3];
-      l4_planes(L, tab);
-    } else {
-      l3_planes(L, tab);
+  if constexpr (B1) {
+    for (int r = w; r < nrows; r += kWaves) {
+      const int p0 = rp_lds[r], p1 = rp_lds[r + 1];
+      const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
+      float sum = 0.f;
+      for (int p = p0 + lane; p < pm; p += 64) {
+        const uint32_t e = ent_lds[p - A0];
+        sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
+      }
+      for (int p = max(p0, Acap) + lane; p < p1; p += 64) {
+        const uint32_t e = entries[p];
+        sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
+      }
+      sum = wave_sum(sum);
+      if (lane == 0) csr[r] = sum;
     }
   } else {
-    tab[0] = 0;
-  }
-
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int gi = g0; gi < g1; gi += PF) {
+    // x is staged transposed, KC columns per pass (plus one zero column), so
+    // that the NB activations of one column are NB*2 contiguous bytes.  Each
+    // DPP row of 16 lanes takes one CSR row (four rows per wave at a time); a
+    // lane takes every 16th entry of its row, reads the entry's NB
+    // activations with 16-byte LDS loads and keeps NB partial sums, which four
+    // DPP steps add up across the 16 lanes.
+    constexpr int NP = NB / 2;
+    const int sl = lane & 15, rr = lane >> 4;
+    for (int c0 = 0; c0 < K; c0 += KC) {
+      const int kc = min(KC, K - c0);
+      if (c0) __syncthreads();
+      // piece i = (k8, pair): 8 columns of batch rows 2 pair and 2 pair + 1, stored as 8 FP16 pairs
+      const int npieces = (kc / 8) * NP;
+      for (int i0 = threadIdx.x; i0 < npieces; i0 += 4 * 64 * kWaves) {
+        u32x4_t lo[4], hi[4];
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int g = gi + u;
-      if (g < g1) {
-        uint32_t am[F::n_mfma][4];
-        decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 64 * kWaves;
+          const int pr = i % NP, k8 = i / NP;
+          const int off = i < npieces ? ((2 * pr) * K + c0 + 8 * k8) * 2 : (int)kOutOfRange;
+          lo[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+          hi[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, off == (int)kOutOfRange ? off : off + K * 2, 0, 0);
+        }
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const half8_t bx = __builtin_bit_cast(half8_t, xr[u][s2]);
-          acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
-          if constexpr (!F::lut) acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 64 * kWaves;
+          if (i < npieces) {
+            uint32_t* d = xT + 8 * (i / NP) * NP + i % NP;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              d[(2 * j) * NP] = perm(hi[u][j], lo[u][j], 0x05040100u);
+              d[(2 * j + 1) * NP] = perm(hi[u][j], lo[u][j], 0x07060302u);
+            }
+          }
         }
       }
-      issue(u, g + PF);
-    }
-  }
-  // acc: row 4*(lane/16) + r, batch column lane % 16
+      if (threadIdx.x < NP) xT[kc * NP + threadIdx.x] = 0u;  // the zero column
+      __syncthreads();
+      for (int j0 = 0; w + 16 * j0 < nrows; j0 += 4) {
+        const int r = w + 16 * (j0 + rr);  // this DPP row's CSR row (may be past the end)
+        const bool real = r < nrows;
+        const int p0 = real ? rp_lds[r] : 0, p1 = real ? rp_lds[r + 1] : 0;
+        const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
+        float an[NB];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) part[w][(4 * (lane >> 4) + r) * 16 + n] = acc[r];
-  __syncthreads();
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-    const int m = i >> 4, c = i & 15, row = 16 * t + m;
-    if (c < B && row < M) {
-      float v = 0.f;
-      for (int ww = 0; ww < nw; ++ww) v += part[ww][i];
-      y[(size_t)c * M + row] = v;
-    }
-  }
-}
-
-// Outliers at batch 8 / 16: y[n][r] += sum_p value_p * x[n][col_p].  A
-// workgroup owns a run of rows.  x is staged transposed in LDS, KC columns at
-// a time, so one entry meets all batch rows in one place; lane (n, slot) of a
-// wave takes batch row n of entry slot.  Every y element is updated by exactly
-// one lane, after the dense kernel on the same stream: no atomics, fixed order.
-template <int NB>
-__global__ void __launch_bounds__(256)
-k_csr_bn(const int32_t* __restrict__ row_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x,
-         float* __restrict__ y, int M, int K, int B, int rows_per_wg, int KC) {
-  constexpr int SL = 64 / NB;           // entry slots per wave instruction
-  constexpr int kRowsPerWave = 8;
-  extern __shared__ uint16_t xT[];      // [KC][NB]
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int n = lane % NB, sl = lane / NB;
-  const int R0 = blockIdx.x * rows_per_wg;
-  const int R1 = min(M, R0 + rows_per_wg);
-  float acc[kRowsPerWave];
-#pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) acc[j] = 0.f;
-  for (int c0 = 0; c0 < K; c0 += KC) {
-    const int kc = min(KC, K - c0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kc * NB; i += blockDim.x) {
-      const int nn = i / kc, k = i - nn * kc;  // read x row-wise, write transposed
-      xT[k * NB + nn] = nn < B ? x[(size_t)nn * K + c0 + k] : (uint16_t)0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kRowsPerWave; ++j) {
-      const int r = R0 + w + 4 * j;
-      if (r < R1) {
-        const int p1 = row_ptr[r + 1];
-        for (int p = row_ptr[r] + sl; p < p1; p += SL) {
-          const uint32_t e = entries[p];
+        for (int j = 0; j < NB; ++j) an[j] = 0.f;
+        auto term = [&](uint32_t e) {
           const int col = (int)(e & 0xFFFFu) - c0;
-          if (col >= 0 && col < kc) acc[j] = dot2(e >> 16, (uint32_t)xT[col * NB + n], acc[j]);
+          const int c = col >= 0 && col < kc ? col : kc;  // out of this pass: the zero column
+          const uint32_t vlo = e >> 16, vhi = e & 0xFFFF0000u;
+#pragma unroll
+          for (int h = 0; h < NB / 8; ++h) {
+            const u32x4_t xv = *(const u32x4_t*)(xT + c * NP + 4 * h);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              an[8 * h + 2 * j] = dot2(vlo, xv[j], an[8 * h + 2 * j]);
+              an[8 * h + 2 * j + 1] = dot2(vhi, xv[j], an[8 * h + 2 * j + 1]);
+            }
+          }
+        };
+        for (int p = p0 + sl; p < pm; p += 16) term(ent_lds[p - A0]);
+        for (int p = max(p0, Acap) + sl; p < p1; p += 16) term(entries[p]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          float v = an[j];
+          v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+          v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+          v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror
+          v += dpp_mov<0x140, 0xF>(v);  // row_mirror: every lane of the row holds the sum
+          an[j] = v;
+        }
+        if (real && sl == 0) {
+          float* d = csr + r * NB;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) d[j] = (c0 ? d[j] : 0.f) + an[j];
         }
       }
     }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
+    const int r = i / NB, n = i % NB;
+    const float* pr = part + (r >> 4) * kWaves * 16 * NB + (r & 15) * NB + n;
+    float v = 0.f;
 #pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) {
-    float v = acc[j];
-    for (int o = NB; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    const int r = R0 + w + 4 * j;
-    if (sl == 0 && r < R1 && n < B) y[(size_t)n * M + r] += v;
+    for (int ww = 0; ww < kWaves; ++ww) v += pr[ww * 16 * NB];
+    if constexpr (B1) y[T0 * 16 + r] = v + csr[r];
+    else y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
   }
 }
 
@@ -601,75 +571,74 @@ k_unpack(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int M, in
 }
 
 // ---- launch plumbing --------------------------------------------------------
-constexpr int kMaxGrid = 256;   // one workgroup per CU
-constexpr int kMaxTilesPerWG = 32;
+constexpr int kMaxGrid = 256;  // one workgroup per CU
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr size_t kEntCapBytes = 64 * 1024;  // CSR entries staged per workgroup, at most
 
-int b1_grid(const BlobHeader& h) {
+// Tiles per workgroup are capped so that the per-tile LDS fits.
+int stream_grid(const BlobHeader& h, int nb) {
+  const int max_tw = nb == 1 ? 32 : (nb == 8 ? 12 : 6);
   int g = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
-  const int need = (h.tiles + kMaxTilesPerWG - 1) / kMaxTilesPerWG;
+  const int need = (h.tiles + max_tw - 1) / max_tw;
   return g > need ? g : need;
 }
 
-constexpr size_t kLdsBytes = 160 * 1024;
-constexpr size_t kEntCapBytes = 64 * 1024;  // CSR entries staged per workgroup
-constexpr size_t kCsrStageBytes = 64 * 1024;  // transposed x per staging pass of k_csr_bn
-
-// LDS of everything but the staged CSR entries.
-size_t b1_lds_fixed(const BlobHeader& h, int grid) {
+// LDS of x (batch 1), partials, CSR sums, row_ptr slice and tables.
+size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
   const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
-  return (size_t)h.Kp * 2 + tw * kWaves * 16 * 4 + tw * 16 * 4 + (tw * 16 + 4) * 4 + tw * 16 * tab;
+  const size_t x = nb == 1 ? (size_t)h.Kp * 2 : 0;
+  return x + tw * kWaves * 16 * nb * 4 + tw * 16 * nb * 4 + (tw * 16 + 4) * 4 + tw * 16 * tab;
 }
 
-template <int FMT, int BITS>
-hipError_t launch_b1(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int PF = 8;
+template <int FMT, int BITS, int NB>
+hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+  constexpr int PF = NB == 1 ? 8 : 3;
   const BlobHeader& h = p->h;
-  const int grid = b1_grid(h);
-  const size_t fixed = b1_lds_fixed(h, grid);
-  size_t cap = kLdsBytes - fixed;
+  const int grid = stream_grid(h, NB);
+  const size_t fixed = stream_lds_fixed(h, grid, NB);
+  // The rest of LDS: batch 1 gives it to CSR entries; batch NB gives the
+  // entries about 1.5x a workgroup's average share and the remainder to the
+  // transposed x of one pass (KC columns, a multiple of 32).
+  const size_t rest = kLdsBytes - fixed;
+  size_t cap = rest;
+  int KC = 0;
+  if (NB > 1) {
+    const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
+    const size_t avg = (size_t)((double)h.nnz * (double)(tw * 16) / (double)h.M * 4.0);
+    cap = avg + avg / 2 + 1023;
+    const size_t most = rest - 33 * NB * 2;  // leave room for one pass of 32 columns and the zero column
+    if (cap > most) cap = most;
+  }
   if (cap > kEntCapBytes) cap = kEntCapBytes;
   cap &= ~(size_t)1023;  // whole 1 KiB wave loads
+  if (NB > 1) {
+    KC = (int)((rest - cap) / (NB * 2) - 1) & ~31;
+    if (KC > h.K) KC = h.K;
+    if (KC < 32) return hipErrorInvalidValue;
+  }
+  const size_t lds = fixed + cap + (NB > 1 ? (size_t)(KC + 1) * NB * 2 : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_b1<FMT, BITS, PF>,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, PF, NB>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
-  hipLaunchKernelGGL((k_b1<FMT, BITS, PF>), dim3(grid), dim3(64 * kWaves), fixed + cap, st, p->blob + h.off_codes,
+  hipLaunchKernelGGL((k_stream<FMT, BITS, PF, NB>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
                      (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
-                     meta_bytes, (int)h.nnz, (int)(cap / 4));
+                     meta_bytes, (int)h.nnz, (int)(cap / 4), KC);
   return hipGetLastError();
 }
 
 template <int FMT, int BITS>
-hipError_t launch_bn(const qgemv_plan* p, const uint16_t* x, float* y, int B, hipStream_t st) {
-  constexpr int PF = 3;
-  const BlobHeader& h = p->h;
-  int waves = h.nkb / 4;  // at least 4 K-blocks per wave
-  waves = waves < 1 ? 1 : (waves > kWaves ? kWaves : waves);
-  const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
-  const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
-  hipLaunchKernelGGL((k_bn<FMT, BITS, PF>), dim3(h.tiles), dim3(64 * waves), 0, st, p->blob + h.off_codes,
-                     (const uint32_t*)(p->blob + h.off_meta), x, y, h.M, h.K, h.nkb, codes_bytes, meta_bytes, B);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || h.nnz == 0) return e;
-  const int rows_per_wg = 4 * 8;  // 4 waves x 8 rows
-  const int grid = (h.M + rows_per_wg - 1) / rows_per_wg;
-  const int nb = B <= 8 ? 8 : 16;
-  const int KC = (int)(kCsrStageBytes / (2 * nb));
-  const size_t lds = (size_t)(KC < h.K ? KC : h.K) * nb * 2;
-  const int32_t* rp = (const int32_t*)(p->blob + h.off_rowptr);
-  const uint32_t* ent = (const uint32_t*)(p->blob + h.off_entries);
-  if (nb == 8)
-    hipLaunchKernelGGL((k_csr_bn<8>), dim3(grid), dim3(256), lds, st, rp, ent, x, y, h.M, h.K, B, rows_per_wg, KC);
-  else
-    hipLaunchKernelGGL((k_csr_bn<16>), dim3(grid), dim3(256), lds, st, rp, ent, x, y, h.M, h.K, B, rows_per_wg, KC);
-  return hipGetLastError();
+hipError_t launch_run(const qgemv_plan* p, const uint16_t* x, float* y, int batch, hipStream_t st) {
+  if (batch == 1) return launch_stream<FMT, BITS, 1>(p, x, y, st);
+  if (batch == 8) return launch_stream<FMT, BITS, 8>(p, x, y, st);
+  return launch_stream<FMT, BITS, 16>(p, x, y, st);
 }
 
 template <int FMT, int BITS>
@@ -717,18 +686,13 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
   if (batch != 1 && batch != 8 && batch != 16) return QGEMV_ERR_UNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   const uint16_t* x = (const uint16_t*)x_dev;
-  const bool lut = h->h.format == QGEMV_FMT_LUT, b4 = h->h.bits == 4;
+  const bool b4 = h->h.bits == 4;
   hipError_t e;
-  if (batch == 1) {
-    if (lut) e = b4 ? launch_b1<QGEMV_FMT_LUT, 4>(h, x, y_dev, st) : launch_b1<QGEMV_FMT_LUT, 3>(h, x, y_dev, st);
-    else e = b4 ? launch_b1<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, st) : launch_b1<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, st);
-  } else {
-    if (lut)
-      e = b4 ? launch_bn<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_bn<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
-    else
-      e = b4 ? launch_bn<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, batch, st)
-             : launch_bn<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, batch, st);
-  }
+  if (h->h.format == QGEMV_FMT_LUT)
+    e = b4 ? launch_run<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_run<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
+  else
+    e = b4 ? launch_run<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, batch, st)
+           : launch_run<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, batch, st);
   return hip_status(e);
 }
 
