@@ -618,13 +618,10 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
     if (KC < 32) return hipErrorInvalidValue;
   }
   const size_t lds = fixed + cap + (NB > 1 ? (size_t)(KC + 1) * NB * 2 : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, PF, NB>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per instantiation (thread-safe static initialisation)
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, PF, NB>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
   const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
   hipLaunchKernelGGL((k_stream<FMT, BITS, PF, NB>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
