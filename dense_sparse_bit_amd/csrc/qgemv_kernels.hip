@@ -195,15 +195,35 @@ __device__ __forceinline__ void load_stats(uint32_t (&s)[2], rsrc_t r, uint32_t 
 
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
 
+// LDS fetch-and-add whose wait sits in the same asm block.  Written out
+// because the compiler, not knowing which LDS bytes an in-flight
+// buffer-to-LDS copy writes, would otherwise drain every global load before
+// an LDS atomic.
+__device__ __forceinline__ int lds_fetch_add(int* p, int v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)p;
+  int r;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr), "v"(v) : "memory");
+  return r;
+}
+
+// Workgroup barrier that orders LDS only: outstanding global loads keep
+// running across it (a plain __syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // The streaming kernel.  One workgroup of 16 waves per CU owns the contiguous
-// tile range [T0, T1) and splits its (tile, K-block) pairs -- tile-major, i.e.
-// one contiguous stretch of the blob -- evenly over its waves.  A wave
-// therefore streams one contiguous run of K-blocks through a ring of PF
-// register slots, crossing a tile boundary at most a few times; at each
-// crossing it parks its partial sums for the finished tile in LDS.  After the
-// stream the partials of every output are added in a fixed order, so the
-// output is deterministic.
+// tile range [T0, T1); its (tile, K-block) pairs, tile-major, are one
+// contiguous stretch of the blob.  The waves take that stretch in chunks of
+// PF consecutive K-blocks of one tile, in order, from an LDS counter, and
+// stream each chunk through a ring of PF register slots (the next chunk's
+// loads are issued as the current one is consumed).  Every chunk writes its
+// partial sums to its own LDS slot; after the stream the slots of every output
+// are added in chunk order, so the output does not depend on which wave took
+// which chunk.
 //
 // Batch 1 (NB = 1): x sits in LDS and every lane reads its B operand from
 // there (the same x in all 16 MFMA columns).  The outliers of the
@@ -237,16 +257,26 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   const int T0 = (int)((int64_t)blockIdx.x * tiles / gridDim.x);
   const int T1 = (int)((int64_t)(blockIdx.x + 1) * tiles / gridDim.x);
   const int TW = T1 - T0;
-  const int nblk = TW * nkb;
-  const int g0 = T0 * nkb + w * nblk / kWaves;
-  const int g1 = T0 * nkb + (w + 1) * nblk / kWaves;
+  // Each tile's K-blocks are cut into CPT chunks of up to PF consecutive
+  // blocks; chunk q of the workgroup is chunk q % CPT of tile T0 + q / CPT.
+  // The waves take chunks in order from an LDS counter: a wave that runs ahead
+  // takes more, so all waves end together and the workgroup sweeps its stretch
+  // of the blob front to back.  Each chunk's partial sums go to the chunk's
+  // own LDS slot, so the result does not depend on which wave took what.
+  const int CPT = (nkb + PF - 1) / PF;
+  const int nchunks = TW * CPT;
+  auto chunk_block = [&](int q, int u) -> int {  // blob block index of slot u of chunk q, or -1
+    const int t = q / CPT, j = q - t * CPT;
+    const int kb = j * PF + u;
+    return q < nchunks && kb < nkb ? (T0 + t) * nkb + kb : -1;
+  };
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
-  // LDS: x [Kp] fp16 (batch 1 only) | part [TW][kWaves][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+4]
+  // LDS: x [Kp] fp16 (batch 1 only) | part [TW*CPT][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+4]
   //      | LUT [TW*16][tab_dw] | CSR entries [ent_cap] | x transposed [KC+1][NB/2] FP16 pairs (batch NB only)
   uint16_t* x_lds = (uint16_t*)lds;
   float* part = (float*)(lds + (B1 ? Kp / 2 : 0));
-  float* csr = part + TW * kWaves * 16 * NB;
+  float* csr = part + nchunks * 16 * NB;
   int* rp_lds = (int*)(csr + TW * 16 * NB);
   uint32_t* lut_lds = (uint32_t*)(rp_lds + TW * 16 + 4);  // 16-byte aligned
   uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);
@@ -265,47 +295,70 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   // Prologue: the ring first, then what goes to LDS; all of it is in flight together.
   const uint32_t voff = (uint32_t)lane * 4 * BITS;
   const uint32_t soff = (uint32_t)lane * 8;
+  // What goes to LDS is loaded first: the x slice (batch 1), the row_ptr
+  // slice and the tables, at most 2 + 1 + 1 pieces per thread.  The code
+  // ring is issued right behind, so storing the staged pieces waits for them
+  // alone, and the barrier below (LDS only) lets the ring loads run on: each
+  // wave starts decoding as soon as its first K-block lands.
+  constexpr int kThreads = 64 * kWaves;
+  u32x4_t xs[2];
+  if constexpr (B1) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      xs[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, i < Kp / 8 ? i * 16 : (int)kOutOfRange, 0, 0);
+    }
+  }
+  const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
+  const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                               rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
+                                         : 0;
+  u32x4_t ls = {0u, 0u, 0u, 0u};
+  const int lpieces = F::lut ? TW * 16 * F::tab_dw / 4 : 0;  // 16-byte pieces of the tables
+  if constexpr (F::lut) {
+    const rsrc_t rl = make_rsrc(meta, meta_bytes);
+    ls = __builtin_amdgcn_raw_buffer_load_b128(
+        rl, (int)threadIdx.x < lpieces ? (T0 * 16 * F::tab_dw / 4 + (int)threadIdx.x) * 16 : (int)kOutOfRange, 0, 0);
+  }
+
   uint32_t cb[PF][BITS];
   uint32_t sb[PF][2];
   u32x4_t xr[B1 ? 1 : PF][4];
-  int ikb = g0 % nkb;  // K-block index of the next block to issue
-  auto issue = [&](int u, int g) {
-    const bool in = g < g1;
+  auto issue = [&](int u, int g) {  // g: blob block index, -1 for none
+    const bool in = g >= 0;
     load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
     if constexpr (!F::lut) load_stats(sb[u], rs, in ? (uint32_t)g * 512 + soff : kOutOfRange);
     else sb[u][0] = sb[u][1] = 0;
     if constexpr (!B1) {
-      const uint32_t xo = in && xrow != kOutOfRange && 128 * ikb + xq < K ? xrow + 256u * (uint32_t)ikb : kOutOfRange;
+      const int kbl = g - (g / nkb) * nkb;
+      const uint32_t xo = in && xrow != kOutOfRange && 128 * kbl + xq < K ? xrow + 256u * (uint32_t)kbl : kOutOfRange;
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2)
         xr[u][s2] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo == kOutOfRange ? kOutOfRange : xo + 16u * s2),
                                                           0, 0);
-      ikb = ikb + 1 == nkb ? 0 : ikb + 1;
     }
   };
+  int c = w;  // the first chunk of wave w; later ones come from the counter
 #pragma unroll
-  for (int u = 0; u < PF; ++u) issue(u, g0 + u);
+  for (int u = 0; u < PF; ++u) issue(u, chunk_block(c, u));
 
   const int E0 = row_ptr[T0 * 16];  // outliers of the workgroup: entries [E0, E1)
   const int E1 = row_ptr[T0 * 16 + nrows];
   if constexpr (B1) {
-    for (int i = threadIdx.x; i < Kp / 8; i += 64 * kWaves)
-      ((u32x4_t*)x_lds)[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, i * 16, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < Kp / 8) ((u32x4_t*)x_lds)[i] = xs[k];
+    }
   }
-  {
-    const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
-    for (int i = threadIdx.x; i <= TW * 16; i += 64 * kWaves)
-      rp_lds[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, min(T0 * 16 + i, M) * 4, 0, 0);
-  }
+  if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
   if constexpr (F::lut) {
-    const rsrc_t rl = make_rsrc(meta, meta_bytes);
-    const int n = TW * 16 * F::tab_dw / 4;  // 16-byte pieces
-    for (int i = threadIdx.x; i < n; i += 64 * kWaves)
-      ((u32x4_t*)lut_lds)[i] = __builtin_amdgcn_raw_buffer_load_b128(rl, (T0 * 16 * F::tab_dw / 4 + i) * 16, 0, 0);
+    if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
   }
-  for (int j = lane; j < TW * 16 * NB; j += 64)
-    part[((j / (16 * NB)) * kWaves + w) * 16 * NB + j % (16 * NB)] = 0.f;
-  __syncthreads();
+  for (int j = threadIdx.x; j < nchunks * 16 * NB; j += kThreads) part[j] = 0.f;  // chunks past a short tile end
+  int* chunk_ctr = rp_lds + TW * 16 + 2;  // a spare slot after the row_ptr slice
+  if (threadIdx.x == 0) *chunk_ctr = kWaves;
+  lds_barrier();
 
   // CSR entries [A0, A0 + ent_cap) of the workgroup's run go to LDS, 1 KiB
   // per wave instruction (16 bytes per lane); issued after the barrier so that
@@ -323,8 +376,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
     }
   }
 
-  int tc = g0 / nkb;  // current tile
-  int kb = g0 - tc * nkb;
+  int tc = -1;  // tile whose table is in tab
   uint32_t tab[F::tab_dw];
   auto planes = [&]() {
     if constexpr (F::lut) {
@@ -338,34 +390,23 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       tab[0] = 0;
     }
   };
-  planes();
 
   const uint16_t* xb = x_lds + xq;
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto flush = [&]() {  // acc[r]: row 4*(lane/16) + r of the tile, batch column lane % 16
-    float* sl = part + ((tc - T0) * kWaves + w) * 16 * NB;
-    if constexpr (B1) {
-      if ((lane & 15) == 0)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sl[4 * (lane >> 4) + r] = acc[r];
-    } else {
-      if ((lane & 15) < NB)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sl[(4 * (lane >> 4) + r) * NB + (lane & 15)] = acc[r];
+  while (c < nchunks) {
+    int cn = 0;
+    if (lane == 0) cn = lds_fetch_add(chunk_ctr, 1);
+    cn = __builtin_amdgcn_readfirstlane(cn);
+    const int t = c / CPT;
+    const int kb0 = (c - t * CPT) * PF;
+    if (T0 + t != tc) {
+      tc = T0 + t;
+      planes();
     }
-    acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  };
-  for (int gi = g0; gi < g1; gi += PF) {
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      const int g = gi + u;
-      if (g < g1) {
-        if (kb == nkb) {
-          flush();
-          kb = 0;
-          ++tc;
-          planes();
-        }
+      const int kb = kb0 + u;
+      if (kb < nkb) {
         uint32_t am[F::n_mfma][4];
         decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
 #pragma unroll
@@ -376,12 +417,22 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
           acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
           if constexpr (!F::lut) acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
         }
-        ++kb;
       }
-      issue(u, g + PF);
+      issue(u, chunk_block(cn, u));
     }
+    // acc[r]: row 4*(lane/16) + r of the tile, batch column lane % 16
+    float* sl = part + c * 16 * NB;
+    if constexpr (B1) {
+      if ((lane & 15) == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl[4 * (lane >> 4) + r] = acc[r];
+    } else {
+      if ((lane & 15) < NB)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl[(4 * (lane >> 4) + r) * NB + (lane & 15)] = acc[r];
+    }
+    c = cn;
   }
-  if (g1 > g0) flush();
 
   // Outliers: entries of the LDS run come from LDS, any beyond it from HBM.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -485,10 +536,9 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   __syncthreads();
   for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
     const int r = i / NB, n = i % NB;
-    const float* pr = part + (r >> 4) * kWaves * 16 * NB + (r & 15) * NB + n;
+    const float* pr = part + (r >> 4) * CPT * 16 * NB + (r & 15) * NB + n;
     float v = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) v += pr[ww * 16 * NB];
+    for (int j = 0; j < CPT; ++j) v += pr[j * 16 * NB];
     if constexpr (B1) y[T0 * 16 + r] = v + csr[r];
     else y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
   }
@@ -574,29 +624,42 @@ k_unpack(const uint8_t* __restrict__ codes, uint8_t* __restrict__ out, int M, in
 constexpr int kMaxGrid = 256;  // one workgroup per CU
 constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kEntCapBytes = 64 * 1024;  // CSR entries staged per workgroup, at most
+constexpr size_t kOneWorkgroupLds = kLdsBytes / 2 + 1024;
 
-// Tiles per workgroup are capped so that the per-tile LDS fits.
-int stream_grid(const BlobHeader& h, int nb) {
-  const int max_tw = nb == 1 ? 32 : (nb == 8 ? 12 : 6);
+// LDS per tile of a workgroup: chunk partials, CSR sums, row_ptr entries, table.
+size_t stream_lds_per_tile(const BlobHeader& h, int nb, int pf) {
+  const size_t cpt = (size_t)((h.nkb + pf - 1) / pf);
+  const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
+  return cpt * 16 * nb * 4 + 16 * (size_t)nb * 4 + 16 * 4 + 16 * tab;
+}
+
+// One workgroup per CU, more when the per-tile LDS of 256 workgroups would
+// not fit.  Batch 1 keeps at least 16 KiB for CSR entries; batch NB keeps at
+// least 64 KiB for CSR entries and transposed x.
+int stream_grid(const BlobHeader& h, int nb, int pf) {
+  const size_t x = nb == 1 ? (size_t)h.Kp * 2 : 0;
+  const size_t keep = nb == 1 ? 16 * 1024 : 64 * 1024;
+  size_t max_tw = (kLdsBytes - x - keep - 16) / stream_lds_per_tile(h, nb, pf);
+  if (max_tw > 32) max_tw = 32;
+  if (max_tw < 1) max_tw = 1;
   int g = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
-  const int need = (h.tiles + max_tw - 1) / max_tw;
+  const int need = (int)((h.tiles + max_tw - 1) / max_tw);
   return g > need ? g : need;
 }
 
 // LDS of x (batch 1), partials, CSR sums, row_ptr slice and tables.
-size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb) {
+size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int pf) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-  const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
   const size_t x = nb == 1 ? (size_t)h.Kp * 2 : 0;
-  return x + tw * kWaves * 16 * nb * 4 + tw * 16 * nb * 4 + (tw * 16 + 4) * 4 + tw * 16 * tab;
+  return x + tw * stream_lds_per_tile(h, nb, pf) + 16;  // + the 4 spare row_ptr slots
 }
 
 template <int FMT, int BITS, int NB>
 hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int PF = NB == 1 ? 8 : 3;
+  constexpr int PF = NB == 1 ? 4 : 3;
   const BlobHeader& h = p->h;
-  const int grid = stream_grid(h, NB);
-  const size_t fixed = stream_lds_fixed(h, grid, NB);
+  const int grid = stream_grid(h, NB, PF);
+  const size_t fixed = stream_lds_fixed(h, grid, NB, PF);
   // The rest of LDS: batch 1 gives it to CSR entries; batch NB gives the
   // entries about 1.5x a workgroup's average share and the remainder to the
   // transposed x of one pass (KC columns, a multiple of 32).
@@ -617,7 +680,9 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
     if (KC > h.K) KC = h.K;
     if (KC < 32) return hipErrorInvalidValue;
   }
-  const size_t lds = fixed + cap + (NB > 1 ? (size_t)(KC + 1) * NB * 2 : 0);
+  size_t lds = fixed + cap + (NB > 1 ? (size_t)(KC + 1) * NB * 2 : 0);
+  // More than half of LDS keeps a second workgroup off the CU: one per CU.
+  if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
   // once per instantiation (thread-safe static initialisation)
   static const hipError_t attr = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, PF, NB>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
