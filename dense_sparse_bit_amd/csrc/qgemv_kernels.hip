@@ -242,7 +242,7 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kWaves = 16;
 constexpr uint32_t kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), no wait on the other counters
 
-template <int FMT, int BITS, int PF, int NB>
+template <int FMT, int BITS, int CH, int NR, int NB>
 __global__ void __launch_bounds__(64 * kWaves)
 k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
          const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
@@ -250,6 +250,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   using F = Fmt<FMT, BITS>;
   constexpr int BB = 256 * BITS;
   constexpr bool B1 = NB == 1;
+  constexpr int PF = CH * NR;  // ring slots: NR chunks of CH K-blocks in flight per wave
   extern __shared__ uint32_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -257,18 +258,27 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   const int T0 = (int)((int64_t)blockIdx.x * tiles / gridDim.x);
   const int T1 = (int)((int64_t)(blockIdx.x + 1) * tiles / gridDim.x);
   const int TW = T1 - T0;
-  // Each tile's K-blocks are cut into CPT chunks of up to PF consecutive
+  // Each tile's K-blocks are cut into CPT chunks of up to CH consecutive
   // blocks; chunk q of the workgroup is chunk q % CPT of tile T0 + q / CPT.
   // The waves take chunks in order from an LDS counter: a wave that runs ahead
   // takes more, so all waves end together and the workgroup sweeps its stretch
-  // of the blob front to back.  Each chunk's partial sums go to the chunk's
-  // own LDS slot, so the result does not depend on which wave took what.
-  const int CPT = (nkb + PF - 1) / PF;
+  // of the blob front to back.  A wave keeps NR chunks in flight.  Each
+  // chunk's partial sums go to the chunk's own LDS slot, so the result does
+  // not depend on which wave took what.
+  const int CPT = (nkb + CH - 1) / CH;
   const int nchunks = TW * CPT;
-  auto chunk_block = [&](int q, int u) -> int {  // blob block index of slot u of chunk q, or -1
-    const int t = q / CPT, j = q - t * CPT;
-    const int kb = j * PF + u;
-    return q < nchunks && kb < nkb ? (T0 + t) * nkb + kb : -1;
+  // Chunk q: tile T0 + q / CPT, K-blocks kb0 .. kb0 + nv - 1, blob block index g0 of the first.
+  struct Chunk {
+    int q, t, kb0, g0, nv;
+  };
+  auto chunk_at = [&](int q) -> Chunk {
+    Chunk k;
+    k.q = q;
+    k.t = q / CPT;
+    k.kb0 = (q - k.t * CPT) * CH;
+    k.g0 = (T0 + k.t) * nkb + k.kb0;
+    k.nv = q < nchunks ? min(CH, nkb - k.kb0) : 0;
+    return k;
   };
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
@@ -338,9 +348,12 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
                                                           0, 0);
     }
   };
-  int c = w;  // the first chunk of wave w; later ones come from the counter
+  // The first chunk of wave w goes to ring half 0 now; the others come from
+  // the counter once it is set up.
+  Chunk ck[NR];
+  ck[0] = chunk_at(w);
 #pragma unroll
-  for (int u = 0; u < PF; ++u) issue(u, chunk_block(c, u));
+  for (int u = 0; u < CH; ++u) issue(u, u < ck[0].nv ? ck[0].g0 + u : -1);
 
   const int E0 = row_ptr[T0 * 16];  // outliers of the workgroup: entries [E0, E1)
   const int E1 = row_ptr[T0 * 16 + nrows];
@@ -351,7 +364,6 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       if (i < Kp / 8) ((u32x4_t*)x_lds)[i] = xs[k];
     }
   }
-  if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
   if constexpr (F::lut) {
     if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
   }
@@ -360,12 +372,17 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   if (threadIdx.x == 0) *chunk_ctr = kWaves;
   lds_barrier();
 
-  // CSR entries [A0, A0 + ent_cap) of the workgroup's run go to LDS, 1 KiB
-  // per wave instruction (16 bytes per lane); issued after the barrier so that
-  // nothing waits on them before the stream ends.
+  // Set-up the dense stream does not need, done by each wave after its first
+  // chunk (or after the stream if it had none), when the row_ptr values have
+  // long arrived: the row_ptr slice goes to LDS, and the CSR entries
+  // [A0, A0 + ent_cap) of the workgroup's run are copied from HBM straight
+  // into LDS, 1 KiB per wave instruction (16 bytes per lane).  Both are first
+  // read after the barrier that ends the stream.
   const int A0 = E0 & ~3;
   const int Acap = min(E1, A0 + ent_cap);
-  {
+  bool late_done = false;
+  auto late_setup = [&]() {
+    if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
     const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
     const int pieces = (Acap - A0 + 3) >> 2;
     for (int i = w; 64 * i < pieces; i += kWaves) {
@@ -374,6 +391,19 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
         __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(ent_lds + 256 * i), 16,
                                                  (A0 + 4 * piece) * 4, 0, 0, 0);
     }
+    late_done = true;
+  };
+
+  auto next_chunk = [&]() -> Chunk {
+    int q = 0;
+    if (lane == 0) q = lds_fetch_add(chunk_ctr, 1);
+    return chunk_at(__builtin_amdgcn_readfirstlane(q));
+  };
+#pragma unroll
+  for (int r = 1; r < NR; ++r) {
+    ck[r] = next_chunk();
+#pragma unroll
+    for (int u = 0; u < CH; ++u) issue(r * CH + u, u < ck[r].nv ? ck[r].g0 + u : -1);
   }
 
   int tc = -1;  // tile whose table is in tab
@@ -392,47 +422,55 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   };
 
   const uint16_t* xb = x_lds + xq;
-  while (c < nchunks) {
-    int cn = 0;
-    if (lane == 0) cn = lds_fetch_add(chunk_ctr, 1);
-    cn = __builtin_amdgcn_readfirstlane(cn);
-    const int t = c / CPT;
-    const int kb0 = (c - t * CPT) * PF;
-    if (T0 + t != tc) {
-      tc = T0 + t;
-      planes();
-    }
-    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // Chunks are taken in increasing order, so once ck[0] is past the end every
+  // later one is too.
+  while (ck[0].q < nchunks) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int kb = kb0 + u;
-      if (kb < nkb) {
-        uint32_t am[F::n_mfma][4];
-        decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
+    for (int r = 0; r < NR; ++r) {
+      const Chunk cur = ck[r];
+      const Chunk nx = next_chunk();
+      const bool live = cur.q < nchunks;
+      if (live && T0 + cur.t != tc) {
+        tc = T0 + cur.t;
+        planes();
+      }
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          half8_t bx;
-          if constexpr (B1) bx = *(const half8_t*)(xb + kb * kBlockK + 8 * s2);
-          else bx = __builtin_bit_cast(half8_t, xr[u][s2]);
-          acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
-          if constexpr (!F::lut) acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+      for (int u = 0; u < CH; ++u) {
+        const int kb = cur.kb0 + u;
+        if (u < cur.nv) {
+          uint32_t am[F::n_mfma][4];
+          decode_chunk<FMT, BITS>(cb[r * CH + u], sb[r * CH + u], tab, am);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            half8_t bx;
+            if constexpr (B1) bx = *(const half8_t*)(xb + kb * kBlockK + 8 * s2);
+            else bx = __builtin_bit_cast(half8_t, xr[r * CH + u][s2]);
+            acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
+            if constexpr (!F::lut)
+              acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+          }
+        }
+        issue(r * CH + u, u < nx.nv ? nx.g0 + u : -1);
+      }
+      // acc[r]: row 4*(lane/16) + r of the tile, batch column lane % 16
+      if (live) {
+        float* sl = part + cur.q * 16 * NB;
+        if constexpr (B1) {
+          if ((lane & 15) == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sl[4 * (lane >> 4) + i] = acc[i];
+        } else {
+          if ((lane & 15) < NB)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sl[(4 * (lane >> 4) + i) * NB + (lane & 15)] = acc[i];
         }
       }
-      issue(u, chunk_block(cn, u));
+      ck[r] = nx;
     }
-    // acc[r]: row 4*(lane/16) + r of the tile, batch column lane % 16
-    float* sl = part + c * 16 * NB;
-    if constexpr (B1) {
-      if ((lane & 15) == 0)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sl[4 * (lane >> 4) + r] = acc[r];
-    } else {
-      if ((lane & 15) < NB)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sl[(4 * (lane >> 4) + r) * NB + (lane & 15)] = acc[r];
-    }
-    c = cn;
+    if (!late_done) late_setup();
   }
+  if (!late_done) late_setup();
 
   // Outliers: entries of the LDS run come from LDS, any beyond it from HBM.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -656,10 +694,11 @@ size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int pf) {
 
 template <int FMT, int BITS, int NB>
 hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int PF = NB == 1 ? 4 : 3;
+  constexpr int CH = NB == 1 ? 4 : 3;  // K-blocks per chunk
+  constexpr int NR = 1;                // chunks in flight per wave
   const BlobHeader& h = p->h;
-  const int grid = stream_grid(h, NB, PF);
-  const size_t fixed = stream_lds_fixed(h, grid, NB, PF);
+  const int grid = stream_grid(h, NB, CH);
+  const size_t fixed = stream_lds_fixed(h, grid, NB, CH);
   // The rest of LDS: batch 1 gives it to CSR entries; batch NB gives the
   // entries about 1.5x a workgroup's average share and the remainder to the
   // transposed x of one pass (KC columns, a multiple of 32).
@@ -684,12 +723,12 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
   // More than half of LDS keeps a second workgroup off the CU: one per CU.
   if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
   // once per instantiation (thread-safe static initialisation)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, PF, NB>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, CH, NR, NB>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
   const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
-  hipLaunchKernelGGL((k_stream<FMT, BITS, PF, NB>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
+  hipLaunchKernelGGL((k_stream<FMT, BITS, CH, NR, NB>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
                      (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
                      meta_bytes, (int)h.nnz, (int)(cap / 4), KC);
