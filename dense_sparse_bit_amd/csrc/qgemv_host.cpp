@@ -276,20 +276,23 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
 
   uint8_t* meta = blob + h.off_meta;
   if (w->format == QGEMV_FMT_UNIFORM) {
+    // per (tile, K-block): z plane [16 rows][8 groups], then s plane [4 group pairs][16 rows][2]
     const int G = K / w->group_size;
     for (int t = 0; t < h.tiles; ++t)
       for (int b = 0; b < nkb; ++b) {
-        uint32_t* m32 = (uint32_t*)(meta + ((size_t)t * nkb + b) * h.meta_unit_bytes);
-        for (int l = 0; l < 64; ++l) {
-          const int row = t * kTileRows + l % 16;
-          for (int q = 0; q < 2; ++q) {
-            const int g = (b * kBlockK + 32 * (l / 16)) / 16 + q;
-            uint32_t v = 0;
-            if (row < M && g < G) {
-              const size_t gi = (size_t)row * G + g;
-              v = (uint32_t)w->scales[gi] | ((uint32_t)w->zeros[gi] << 16);
+        uint16_t* zp = (uint16_t*)(meta + ((size_t)t * nkb + b) * h.meta_unit_bytes);
+        uint16_t* sp = zp + kTileRows * 8;
+        for (int r = 0; r < kTileRows; ++r) {
+          const int row = t * kTileRows + r;
+          for (int g = 0; g < 8; ++g) {
+            const int gg = b * 8 + g;
+            uint16_t sv = 0, zv = 0;
+            if (row < M && gg < G) {
+              sv = w->scales[(size_t)row * G + gg];
+              zv = w->zeros[(size_t)row * G + gg];
             }
-            m32[2 * l + q] = v;
+            zp[r * 8 + g] = zv;
+            sp[(g / 2) * 32 + r * 2 + (g % 2)] = sv;
           }
         }
       }

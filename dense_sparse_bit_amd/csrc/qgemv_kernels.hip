@@ -98,12 +98,56 @@ template <int FMT, int BITS>
 struct Fmt {
   static constexpr bool lut = FMT == QGEMV_FMT_LUT;
   static constexpr int tab_dw = lut ? (BITS == 4 ? 8 : 4) : 1;
-  static constexpr int n_mfma = lut ? 4 : 8;   // per K-block
+  static constexpr int n_mfma = lut ? 4 : 8;   // per K-block, split-scale decode
 };
+
+// Uniform codes of one lane chunk as exact FP16 pairs (q - z): pair m holds
+// chunk codes 2m, 2m+1.  zw holds the zero points of the chunk's two groups
+// (codes 0-15 and 16-31) in its low and high half.
+template <int BITS>
+__device__ __forceinline__ void uniform_qz(const uint32_t (&c)[BITS], uint32_t zw, uint32_t (&qz)[16]) {
+  uint32_t cz[2][3];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint32_t zb = g ? zw >> 16 : zw & 0xFFFFu;
+    cz[g][0] = hsplat_neg_sum(zb, 1024.f);
+    cz[g][1] = hsplat_neg_sum(zb, BITS == 4 ? 64.f : 128.f);
+    cz[g][2] = hsplat_neg_sum(zb, 16.f);
+  }
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int g = d / 2;
+      uint32_t h[4];
+      u4_slots(c[d], h);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        qz[4 * d + t] = (t & 1) ? to_qz(h[t], cz[g][1], (_Float16)0.0625f) : to_qz(h[t], cz[g][0], (_Float16)1.0f);
+    }
+  } else {
+    uint32_t h[3][5];
+    u3_slots(c[0], h[0]);
+    u3_slots(c[1], h[1]);
+    u3_slots(c[2], h[2]);
+    const uint32_t hs = u3_spare(c[0], c[1], c[2]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int g = m < 8 ? 0 : 1;
+      if (m == 15) {
+        qz[m] = to_qz(hs, cz[g][0], (_Float16)1.0f);
+      } else {
+        const int d = m / 5, t = m % 5;
+        if (t == 0 || t == 3) qz[m] = to_qz(h[d][t], cz[g][0], (_Float16)1.0f);
+        else if (t == 2) qz[m] = to_qz(h[d][t], cz[g][2], (_Float16)0.015625f);
+        else qz[m] = to_qz(h[d][t], cz[g][1], (_Float16)0.125f);
+      }
+    }
+  }
+}
 
 // Decode one lane chunk into MFMA A operands.
 //   LUT:     a[i][0..3] for step i = 0..3
-//   UNIFORM: a[i] = hi part, a[4 + i] = lo part
+//   UNIFORM: a[i] = s_hi * (q - z), a[4 + i] = s_lo * (q - z); st[g] = scale | zero << 16 of group g
 template <int FMT, int BITS>
 __device__ __forceinline__ void decode_chunk(const uint32_t (&c)[BITS], const uint32_t (&st)[2],
                                              const uint32_t (&tab)[Fmt<FMT, BITS>::tab_dw],
@@ -122,49 +166,15 @@ __device__ __forceinline__ void decode_chunk(const uint32_t (&c)[BITS], const ui
 #pragma unroll
     for (int q = 0; q < 8; ++q) l3_lookup(tab, sel[q], a[q / 2][2 * (q % 2)], a[q / 2][2 * (q % 2) + 1]);
   } else {
-    uint32_t shi[2], slo[2], cz[2][3];
+    uint32_t qz[16], shi[2], slo[2];
+    uniform_qz<BITS>(c, (st[0] >> 16) | (st[1] & 0xFFFF0000u), qz);
+    scale_split(st[0], shi[0], slo[0]);
+    scale_split(st[1], shi[1], slo[1]);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      scale_split(st[g], shi[g], slo[g]);
-      const uint32_t zb = st[g] >> 16;
-      cz[g][0] = hsplat_neg_sum(zb, 1024.f);
-      cz[g][1] = hsplat_neg_sum(zb, BITS == 4 ? 64.f : 128.f);
-      cz[g][2] = hsplat_neg_sum(zb, 16.f);
-    }
-    if constexpr (BITS == 4) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int g = d / 2;
-        uint32_t h[4];
-        u4_slots(c[d], h);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t qz = (t & 1) ? to_qz(h[t], cz[g][1], (_Float16)0.0625f) : to_qz(h[t], cz[g][0], (_Float16)1.0f);
-          a[d][t] = hmul(qz, shi[g]);
-          a[4 + d][t] = hmul(qz, slo[g]);
-        }
-      }
-    } else {
-      uint32_t h[3][5];
-      u3_slots(c[0], h[0]);
-      u3_slots(c[1], h[1]);
-      u3_slots(c[2], h[2]);
-      const uint32_t hs = u3_spare(c[0], c[1], c[2]);
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int g = m < 8 ? 0 : 1;
-        uint32_t qz;
-        if (m == 15) {
-          qz = to_qz(hs, cz[g][0], (_Float16)1.0f);
-        } else {
-          const int d = m / 5, t = m % 5;
-          if (t == 0 || t == 3) qz = to_qz(h[d][t], cz[g][0], (_Float16)1.0f);
-          else if (t == 2) qz = to_qz(h[d][t], cz[g][2], (_Float16)0.015625f);
-          else qz = to_qz(h[d][t], cz[g][1], (_Float16)0.125f);
-        }
-        a[m / 4][m % 4] = hmul(qz, shi[g]);
-        a[4 + m / 4][m % 4] = hmul(qz, slo[g]);
-      }
+    for (int m = 0; m < 16; ++m) {
+      const int g = m < 8 ? 0 : 1;
+      a[m / 4][m % 4] = hmul(qz[m], shi[g]);
+      a[4 + m / 4][m % 4] = hmul(qz[m], slo[g]);
     }
   }
 }
@@ -282,10 +292,10 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   };
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
-  // LDS: x [Kp] fp16 (batch 1 only) | part [TW*CPT][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+4]
+  // LDS: x [Kp+8] fp16 (batch 1 only) | part [TW*CPT][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+4]
   //      | LUT [TW*16][tab_dw] | CSR entries [ent_cap] | x transposed [KC+1][NB/2] FP16 pairs (batch NB only)
-  uint16_t* x_lds = (uint16_t*)lds;
-  float* part = (float*)(lds + (B1 ? Kp / 2 : 0));
+  uint16_t* x_lds = (uint16_t*)lds;  // batch 1: x, then 16 zero bytes
+  float* part = (float*)(lds + (B1 ? Kp / 2 + 4 : 0));
   float* csr = part + nchunks * 16 * NB;
   int* rp_lds = (int*)(csr + TW * 16 * NB);
   uint32_t* lut_lds = (uint32_t*)(rp_lds + TW * 16 + 4);  // 16-byte aligned
@@ -304,7 +314,15 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
 
   // Prologue: the ring first, then what goes to LDS; all of it is in flight together.
   const uint32_t voff = (uint32_t)lane * 4 * BITS;
-  const uint32_t soff = (uint32_t)lane * 8;
+  // Uniform statistics of a K-block (see qgemv_layout.h): the z pair of the
+  // lane's two groups, and either the s pair (split-scale decode, batch NB) or
+  // the scales of group lane % 16 for rows 4*(lane/16) .. +3 (batch 1).
+  constexpr bool UG1 = B1 && !F::lut;  // batch-1 uniform: MFMA columns are the K-block's groups
+  constexpr int SBW = UG1 ? 5 : 2;
+  const uint32_t zoff = (uint32_t)(lane & 15) * 16 + (uint32_t)(lane >> 4) * 4;
+  const uint32_t spoff = 256 + (uint32_t)(lane >> 4) * 64 + (uint32_t)(lane & 15) * 4;
+  const uint32_t sqoff = (lane & 15) < 8 ? 256 + (uint32_t)((lane & 15) >> 1) * 64 + (uint32_t)(lane >> 4) * 16
+                                         : kOutOfRange;
   // What goes to LDS is loaded first: the x slice (batch 1), the row_ptr
   // slice and the tables, at most 2 + 1 + 1 pieces per thread.  The code
   // ring is issued right behind, so storing the staged pieces waits for them
@@ -332,13 +350,24 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   }
 
   uint32_t cb[PF][BITS];
-  uint32_t sb[PF][2];
+  uint32_t sb[PF][SBW];
   u32x4_t xr[B1 ? 1 : PF][4];
   auto issue = [&](int u, int g) {  // g: blob block index, -1 for none
     const bool in = g >= 0;
     load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
-    if constexpr (!F::lut) load_stats(sb[u], rs, in ? (uint32_t)g * 512 + soff : kOutOfRange);
-    else sb[u][0] = sb[u][1] = 0;
+    if constexpr (!F::lut) {
+      const uint32_t mb = in ? (uint32_t)g * 512 : kOutOfRange;
+      sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + zoff : kOutOfRange), 0, 0);
+      if constexpr (UG1) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (int)(in && sqoff != kOutOfRange ? mb + sqoff : kOutOfRange), 0, 0);
+        sb[u][1] = v[0]; sb[u][2] = v[1]; sb[u][3] = v[2]; sb[u][4] = v[3];
+      } else {
+        sb[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + spoff : kOutOfRange), 0, 0);
+      }
+    } else {
+      sb[u][0] = sb[u][1] = 0;
+    }
     if constexpr (!B1) {
       const int kbl = g - (g / nkb) * nkb;
       const uint32_t xo = in && xrow != kOutOfRange && 128 * kbl + xq < K ? xrow + 256u * (uint32_t)kbl : kOutOfRange;
@@ -363,6 +392,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       const int i = threadIdx.x + k * kThreads;
       if (i < Kp / 8) ((u32x4_t*)x_lds)[i] = xs[k];
     }
+    if (threadIdx.x < 4) ((uint32_t*)(x_lds + Kp))[threadIdx.x] = 0u;
   }
   if constexpr (F::lut) {
     if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
@@ -422,6 +452,8 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   };
 
   const uint16_t* xb = x_lds + xq;
+  const int jn = (lane & 15) - 2 * (lane >> 4);  // batch-1 uniform: the step pair that feeds this lane's column
+  const uint32_t sh = 16u * (uint32_t)(lane & 1);
   // Chunks are taken in increasing order, so once ck[0] is past the end every
   // later one is too.
   while (ck[0].q < nchunks) {
@@ -438,20 +470,58 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int kb = cur.kb0 + u;
+        const int sl = r * CH + u;
         if (u < cur.nv) {
-          uint32_t am[F::n_mfma][4];
-          decode_chunk<FMT, BITS>(cb[r * CH + u], sb[r * CH + u], tab, am);
+          if constexpr (UG1) {
+            // Batch-1 uniform: A = exact (q - z), B = x masked so that MFMA column n
+            // sees only group n of the K-block (step s2 covers groups 2*(lane/16) +
+            // s2/2 in lane group lane/16).  cg[i] = sum over group lane % 16 of
+            // (q - z) x for row 4*(lane/16) + i; its scale is applied in fp32.
+            uint32_t qz[16];
+            uniform_qz<BITS>(cb[sl], sb[sl][0], qz);
+            floatx4_t cg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) {
-            half8_t bx;
-            if constexpr (B1) bx = *(const half8_t*)(xb + kb * kBlockK + 8 * s2);
-            else bx = __builtin_bit_cast(half8_t, xr[r * CH + u][s2]);
-            acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
-            if constexpr (!F::lut)
-              acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+            for (int s2 = 0; s2 < 4; ++s2) {
+              const bool on = (s2 >> 1) == jn;
+              const half8_t bx = *(const half8_t*)(on ? xb + kb * kBlockK + 8 * s2 : x_lds + Kp);
+              cg = mfma(h8(qz[4 * s2], qz[4 * s2 + 1], qz[4 * s2 + 2], qz[4 * s2 + 3]), bx, cg);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(sb[sl][1 + i] >> sh));
+              acc[i] += (float)sc * cg[i];
+            }
+          } else {
+            uint32_t am[F::n_mfma][4];
+            if constexpr (F::lut) {
+              decode_chunk<FMT, BITS>(cb[sl], sb[sl], tab, am);
+            } else {
+              const uint32_t st[2] = {perm(sb[sl][0], sb[sl][1], 0x05040100u),
+                                      perm(sb[sl][0], sb[sl][1], 0x07060302u)};
+              decode_chunk<FMT, BITS>(cb[sl], st, tab, am);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+              half8_t bx;
+              if constexpr (B1) bx = *(const half8_t*)(xb + kb * kBlockK + 8 * s2);
+              else bx = __builtin_bit_cast(half8_t, xr[sl][s2]);
+              acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
+              if constexpr (!F::lut)
+                acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+            }
           }
         }
-        issue(r * CH + u, u < nx.nv ? nx.g0 + u : -1);
+        issue(sl, u < nx.nv ? nx.g0 + u : -1);
+      }
+      if constexpr (UG1) {  // add the 8 groups (lanes 16j + 0..7) of every row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = acc[i];
+          v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+          v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+          v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror
+          acc[i] = v;
+        }
       }
       // acc[r]: row 4*(lane/16) + r of the tile, batch column lane % 16
       if (live) {
@@ -675,7 +745,7 @@ size_t stream_lds_per_tile(const BlobHeader& h, int nb, int pf) {
 // not fit.  Batch 1 keeps at least 16 KiB for CSR entries; batch NB keeps at
 // least 64 KiB for CSR entries and transposed x.
 int stream_grid(const BlobHeader& h, int nb, int pf) {
-  const size_t x = nb == 1 ? (size_t)h.Kp * 2 : 0;
+  const size_t x = nb == 1 ? (size_t)h.Kp * 2 + 16 : 0;
   const size_t keep = nb == 1 ? 16 * 1024 : 64 * 1024;
   size_t max_tw = (kLdsBytes - x - keep - 16) / stream_lds_per_tile(h, nb, pf);
   if (max_tw > 32) max_tw = 32;
@@ -688,7 +758,7 @@ int stream_grid(const BlobHeader& h, int nb, int pf) {
 // LDS of x (batch 1), partials, CSR sums, row_ptr slice and tables.
 size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int pf) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-  const size_t x = nb == 1 ? (size_t)h.Kp * 2 : 0;
+  const size_t x = nb == 1 ? (size_t)h.Kp * 2 + 16 : 0;  // x and 16 zero bytes
   return x + tw * stream_lds_per_tile(h, nb, pf) + 16;  // + the 4 spare row_ptr slots
 }
 

@@ -36,8 +36,12 @@
 //      byte k of dword 2 is bit 2 of code 24+k (28+k).
 //
 // meta    LUT: per row (tiles*16 rows) the canonical FP16 table, 2^bits entries.
-//         UNIFORM: per (tile, K-block, lane) two dwords, one per 16-code group
-//         of the lane's chunk: FP16 scale (low half) | FP16 zero (high half).
+//         UNIFORM: 512 bytes per (tile, K-block) for its 16 rows x 8 groups of
+//         16 codes: a z plane, FP16 zero points [row][group] (256 B), then an
+//         s plane, FP16 scales [group / 2][row][group % 2] (256 B).  Lane l's
+//         two groups (2*(l/16), 2*(l/16)+1) of row l % 16 are one dword in each
+//         plane; the scales of one group for four consecutive rows are one
+//         16-byte piece of the s plane.
 // row_ptr int32 [M+1] (as given).
 // entries uint32 [nnz]: column (low 16 bits) | FP16 value bits (high 16 bits).
 #pragma once
@@ -47,7 +51,7 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 2;
+constexpr uint32_t kVersion = 3;
 constexpr int kTileRows = 16;
 constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
