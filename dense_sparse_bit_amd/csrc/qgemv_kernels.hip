@@ -764,7 +764,7 @@ size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int pf) {
 
 template <int FMT, int BITS, int NB>
 hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int CH = NB == 1 ? 4 : 3;  // K-blocks per chunk
+  constexpr int CH = NB == 1 ? 2 : 3;  // K-blocks per chunk
   constexpr int NR = 1;                // chunks in flight per wave
   const BlobHeader& h = p->h;
   const int grid = stream_grid(h, NB, CH);
