@@ -1,23 +1,29 @@
 // qgemv_kernels.hip -- gfx950 kernels and the device side of the C ABI.
 //
-// The product runs on 16-row tiles.  In a batch-1 launch one workgroup owns
-// one tile and its KS waves split the K-blocks of that tile:
-//   * each lane streams the 32-code chunks of its row (16 B or 12 B per
-//     K-block, 1 KiB / 768 B contiguous per wave load), through a ring of PF
-//     K-blocks held in registers;
-//   * it turns them into FP16 A operands -- v_perm byte lookups in the row's
-//     table for LUT codes, a magic-number OR plus exact FP16 scaling for
-//     uniform codes -- and issues 16x16x32 MFMAs against x read from LDS (B
-//     operand, the same x in every column), fp32 accumulation;
-//   * the row's CSR outliers are gathered from the same LDS copy of x and
-//     reduced with a DPP wave sum;
-//   * partial sums of the KS waves meet in LDS and are added in a fixed order,
-//     so every output is written once, with no atomics, deterministically.
+// The product runs on 16-row tiles (the M side of a 16x16x32 MFMA) and
+// K-blocks of 128 codes.  Every kernel runs one workgroup of 16 waves per CU;
+// a workgroup owns a contiguous range of tiles, whose (tile, K-block) pairs are
+// one contiguous stretch of the blob.
+//   * k_stream: batch 1, and batch 8 / 16 when x does not fit in LDS.  The
+//     waves take chunks of consecutive K-blocks in order from an LDS counter;
+//     each lane streams the 32-code chunk of its row (16 B or 12 B per
+//     K-block, 1 KiB / 768 B contiguous per wave load) through a register
+//     ring, turns it into FP16 A operands (v_perm byte lookups in the row's
+//     table for LUT codes; exact (q - z) values for uniform codes) and issues
+//     16x16x32 MFMAs with fp32 accumulation.  Batch 1 reads x from LDS;
+//     batch 8 / 16 loads it from L2 next to the codes.
+//   * k_xlds: batch 8 / 16 with x resident in LDS for the whole launch.
+// The CSR outliers of a workgroup's rows are copied into LDS while the dense
+// stream runs and gathered against x in LDS; every output is written once,
+// with no atomics, and partial sums meet in a fixed order, so results are
+// deterministic.
 //
-// Uniform codes: the group scale s is split into s_hi (s with the four low
-// mantissa bits cleared) and s_lo = s - s_hi.  (q - z) * s_hi and (q - z) * s_lo
-// are exact in FP16, so two MFMAs reproduce s * (q - z) * x without rounding
-// the decoded weight.
+// Uniform codes, batch 1: the MFMA columns are the eight groups of a K-block
+// (x masked per column), so each group's sum of (q - z) * x comes out
+// separately and its scale is applied in fp32.  Batch 8 / 16: the group scale
+// s is split into s_hi (s with the four low mantissa bits cleared) and
+// s_lo = s - s_hi; (q - z) * s_hi and (q - z) * s_lo are exact in FP16, so two
+// MFMAs reproduce s * (q - z) * x without rounding the decoded weight.
 
 #include <hip/hip_runtime.h>
 
@@ -186,19 +192,25 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// Cache policy of loads whose bytes are read once (codes, statistics,
+// tables, CSR entries): non-temporal, which streams measurably faster from
+// HBM than the default policy.  x, which every workgroup reads, keeps the
+// default.
+constexpr int kNonTemporal = 2;
+
 // Loads through a range-checked buffer resource: offsets past the range read 0 and touch no memory.
 template <int BITS>
 __device__ __forceinline__ void load_chunk(uint32_t (&c)[BITS], rsrc_t r, uint32_t off) {
   if constexpr (BITS == 4) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
     c[0] = v[0]; c[1] = v[1]; c[2] = v[2]; c[3] = v[3];
   } else {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)off, 0, kNonTemporal);
     c[0] = v[0]; c[1] = v[1]; c[2] = v[2];
   }
 }
 __device__ __forceinline__ void load_stats(uint32_t (&s)[2], rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
   s[0] = v[0];
   s[1] = v[1];
 }
@@ -214,6 +226,20 @@ __device__ __forceinline__ int lds_fetch_add(int* p, int v) {
   int r;
   asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr), "v"(v) : "memory");
   return r;
+}
+
+// Plain LDS read and write of a flag another wave updates, addressed as LDS
+// (a volatile generic pointer would become a flat access, whose wait also
+// drains the wave's global loads).
+__device__ __forceinline__ int lds_read_flag(const int* p) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const int*)p;
+  int r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_write_flag(int* p, int v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)p;
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
 // Workgroup barrier that orders LDS only: outstanding global loads keep
@@ -281,23 +307,28 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   struct Chunk {
     int q, t, kb0, g0, nv;
   };
+  // Batch NB: each workgroup starts its tiles' K sweep at its own chunk, so
+  // that the workgroups do not all read the same x lines from L2 at once.
+  const int rot = B1 ? 0 : (int)(blockIdx.x % (unsigned)CPT);
   auto chunk_at = [&](int q) -> Chunk {
     Chunk k;
     k.q = q;
     k.t = q / CPT;
-    k.kb0 = (q - k.t * CPT) * CH;
+    int j = q - k.t * CPT + rot;
+    if (j >= CPT) j -= CPT;
+    k.kb0 = j * CH;
     k.g0 = (T0 + k.t) * nkb + k.kb0;
     k.nv = q < nchunks ? min(CH, nkb - k.kb0) : 0;
     return k;
   };
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
-  // LDS: x [Kp+8] fp16 (batch 1 only) | part [TW*CPT][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+4]
+  // LDS: x [Kp+8] fp16 (batch 1 only) | part [TW*CPT][16][NB] | csr [TW*16][NB] (batch NB only) | row_ptr [TW*16+4]
   //      | LUT [TW*16][tab_dw] | CSR entries [ent_cap] | x transposed [KC+1][NB/2] FP16 pairs (batch NB only)
   uint16_t* x_lds = (uint16_t*)lds;  // batch 1: x, then 16 zero bytes
   float* part = (float*)(lds + (B1 ? Kp / 2 + 4 : 0));
-  float* csr = part + nchunks * 16 * NB;
-  int* rp_lds = (int*)(csr + TW * 16 * NB);
+  float* csr = part + nchunks * 16 * NB;  // batch NB only
+  int* rp_lds = (int*)(csr + (B1 ? 0 : TW * 16 * NB));
   uint32_t* lut_lds = (uint32_t*)(rp_lds + TW * 16 + 4);  // 16-byte aligned
   uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);
   uint32_t* xT = ent_lds + ent_cap;
@@ -341,12 +372,16 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
                                                rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
                                          : 0;
+  // The bounds [E0, E1) of the workgroup's outliers, in lanes 0 and 1 of
+  // every wave: vector loads, which the LDS barrier below does not wait for
+  // (scalar loads would hold it until they return).
+  const int ev = lane < 2 ? __builtin_amdgcn_raw_buffer_load_b32(rr, (T0 * 16 + (lane ? nrows : 0)) * 4, 0, 0) : 0;
   u32x4_t ls = {0u, 0u, 0u, 0u};
   const int lpieces = F::lut ? TW * 16 * F::tab_dw / 4 : 0;  // 16-byte pieces of the tables
   if constexpr (F::lut) {
     const rsrc_t rl = make_rsrc(meta, meta_bytes);
     ls = __builtin_amdgcn_raw_buffer_load_b128(
-        rl, (int)threadIdx.x < lpieces ? (T0 * 16 * F::tab_dw / 4 + (int)threadIdx.x) * 16 : (int)kOutOfRange, 0, 0);
+        rl, (int)threadIdx.x < lpieces ? (T0 * 16 * F::tab_dw / 4 + (int)threadIdx.x) * 16 : (int)kOutOfRange, 0, kNonTemporal);
   }
 
   uint32_t cb[PF][BITS];
@@ -357,13 +392,13 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
     load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
     if constexpr (!F::lut) {
       const uint32_t mb = in ? (uint32_t)g * 512 : kOutOfRange;
-      sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + zoff : kOutOfRange), 0, 0);
+      sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + zoff : kOutOfRange), 0, kNonTemporal);
       if constexpr (UG1) {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-            rs, (int)(in && sqoff != kOutOfRange ? mb + sqoff : kOutOfRange), 0, 0);
+            rs, (int)(in && sqoff != kOutOfRange ? mb + sqoff : kOutOfRange), 0, kNonTemporal);
         sb[u][1] = v[0]; sb[u][2] = v[1]; sb[u][3] = v[2]; sb[u][4] = v[3];
       } else {
-        sb[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + spoff : kOutOfRange), 0, 0);
+        sb[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + spoff : kOutOfRange), 0, kNonTemporal);
       }
     } else {
       sb[u][0] = sb[u][1] = 0;
@@ -384,8 +419,6 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
 #pragma unroll
   for (int u = 0; u < CH; ++u) issue(u, u < ck[0].nv ? ck[0].g0 + u : -1);
 
-  const int E0 = row_ptr[T0 * 16];  // outliers of the workgroup: entries [E0, E1)
-  const int E1 = row_ptr[T0 * 16 + nrows];
   if constexpr (B1) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -408,10 +441,12 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   // [A0, A0 + ent_cap) of the workgroup's run are copied from HBM straight
   // into LDS, 1 KiB per wave instruction (16 bytes per lane).  Both are first
   // read after the barrier that ends the stream.
-  const int A0 = E0 & ~3;
-  const int Acap = min(E1, A0 + ent_cap);
+  int A0 = 0, Acap = 0;
   bool late_done = false;
   auto late_setup = [&]() {
+    const int E0 = __builtin_amdgcn_readlane(ev, 0), E1 = __builtin_amdgcn_readlane(ev, 1);
+    A0 = E0 & ~3;
+    Acap = min(E1, A0 + ent_cap);
     if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
     const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
     const int pieces = (Acap - A0 + 3) >> 2;
@@ -419,7 +454,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       const int piece = 64 * i + lane;
       if (piece < pieces)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(ent_lds + 256 * i), 16,
-                                                 (A0 + 4 * piece) * 4, 0, 0, 0);
+                                                 (A0 + 4 * piece) * 4, 0, 0, kNonTemporal);
     }
     late_done = true;
   };
@@ -546,20 +581,43 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
   if constexpr (B1) {
-    for (int r = w; r < nrows; r += kWaves) {
-      const int p0 = rp_lds[r], p1 = rp_lds[r + 1];
-      const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
-      float sum = 0.f;
-      for (int p = p0 + lane; p < pm; p += 64) {
-        const uint32_t e = ent_lds[p - A0];
-        sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
+    // One DPP row of 16 lanes per output row, four rows per wave at a time.
+    // Lane j of a row takes every 16th outlier of the row and every 16th of
+    // the row's chunk partials (chunk order j, j + 16, ...); four DPP steps
+    // add the 16 lanes, and the row's output is written at once.
+    const int sl = lane & 15;
+    for (int r0 = 4 * w; r0 < nrows; r0 += 4 * kWaves) {
+      const int r = r0 + (lane >> 4);
+      float v = 0.f;
+      if (r < nrows) {
+        const int p0 = rp_lds[r], p1 = rp_lds[r + 1];
+        const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
+        int p = p0 + sl;
+        for (; p + 48 < pm; p += 64) {  // four outliers in flight
+          uint32_t e[4], xv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[u] = ent_lds[p + 16 * u - A0];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xv[u] = x_lds[e[u] & 0xFFFFu];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v = dot2(e[u] >> 16, xv[u], v);
+        }
+        for (; p < pm; p += 16) {
+          const uint32_t e = ent_lds[p - A0];
+          v = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], v);
+        }
+        for (int p = max(p0, Acap) + sl; p < p1; p += 16) {
+          const uint32_t e = entries[p];
+          v = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], v);
+        }
+        const float* ps = part + (r >> 4) * CPT * 16 + (r & 15);
+        for (int j = sl; j < CPT; j += 16) v += ps[j * 16];
       }
-      for (int p = max(p0, Acap) + lane; p < p1; p += 64) {
-        const uint32_t e = entries[p];
-        sum = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], sum);
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) csr[r] = sum;
+      v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+      v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+      v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror
+      v += dpp_mov<0x140, 0xF>(v);  // row_mirror: every lane of the row holds the sum
+      if (r < nrows && sl == 0) y[T0 * 16 + r] = v;
     }
   } else {
     // x is staged transposed, KC columns per pass (plus one zero column), so
@@ -641,14 +699,261 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       }
     }
   }
+  if constexpr (!B1) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
+      const int r = i / NB, n = i % NB;
+      const float* pr = part + (r >> 4) * CPT * 16 * NB + (r & 15) * NB + n;
+      float v = 0.f;
+      for (int j = 0; j < CPT; ++j) v += pr[j * 16 * NB];
+      y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Batch 8 / 16 with x resident in LDS, for shapes whose x (NB * Kp * 2 bytes)
+// fits next to the partial sums.  x is copied once into LDS as
+// [Kp / 8][NB][8] FP16: the eight activations of batch row n at columns
+// 8j .. 8j+7 are the 16 bytes at ((j * NB) + n) * 16.  That is one MFMA B
+// operand piece, so each K-step of a K-block reads its B operand with one
+// 16-byte LDS load per lane, and the outlier sums read their activations from
+// the same copy.
+//
+// The workgroup's (tile, K-block) pairs, tile-major, are cut into 16
+// contiguous runs, one per wave; a wave streams its run through a ring of R
+// code slots and keeps one accumulator per tile it touches.  Wave v writes its
+// sums for local tile t to partial slot v + t -- distinct for every (v, t) a
+// run can touch, because the runs are ordered -- and each output adds the
+// slots of the waves covering its tile in wave order, then the outliers, so
+// the result does not depend on timing.
+// ---------------------------------------------------------------------------
+template <int FMT, int BITS, int NB, int R>
+__global__ void __launch_bounds__(64 * kWaves)
+k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
+       const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
+       int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap) {
+  using F = Fmt<FMT, BITS>;
+  constexpr int BB = 256 * BITS;
+  constexpr int NP = NB / 2;
+  extern __shared__ uint32_t lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T0 = (int)((int64_t)blockIdx.x * tiles / gridDim.x);
+  const int T1 = (int)((int64_t)(blockIdx.x + 1) * tiles / gridDim.x);
+  const int TW = T1 - T0;
+  const int nrows = min(TW * 16, M - T0 * 16);
+  const int L = TW * nkb;  // (tile, K-block) pairs of the workgroup
+  const int b0 = w * L / kWaves, b1 = (w + 1) * L / kWaves;  // this wave's run
+
+  // LDS: xs [Kp/8][NB][8] FP16 | slots [TW+15][16][NB] | csr [TW*16][NB] | row_ptr [TW*16+1, padded]
+  //      | runs [16][2] | group counter (padded) | LUT [TW*16][tab_dw] | CSR entries [ent_cap]
+  uint16_t* xs = (uint16_t*)lds;
+  float* slots = (float*)(lds + Kp * NB / 2);
+  float* csr = slots + (TW + 15) * 16 * NB;
+  int* rp_lds = (int*)(csr + TW * 16 * NB);
+  int* runs = rp_lds + ((TW * 16 + 4) & ~3);
+  int* group_ctr = runs + 2 * kWaves;  // CSR row groups taken
+  uint32_t* lut_lds = (uint32_t*)(group_ctr + 4);  // 16-byte aligned
+  uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);
+
+  const rsrc_t rc = make_rsrc(codes, codes_bytes);
+  const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)NB * (uint32_t)K * 2u);
+  const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
+
+  // Prologue.  Small loads first (row_ptr slice, outlier bounds, tables),
+  // then x and the CSR run straight into LDS, then the code ring; all of it
+  // has landed before the barrier, so no LDS copy is pending in the stream.
+  const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                               rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
+                                         : 0;
+  const int ev = lane < 2 ? __builtin_amdgcn_raw_buffer_load_b32(rr, (T0 * 16 + (lane ? nrows : 0)) * 4, 0, 0) : 0;
+  u32x4_t ls = {0u, 0u, 0u, 0u};
+  const int lpieces = F::lut ? TW * 16 * F::tab_dw / 4 : 0;
+  if constexpr (F::lut) {
+    const rsrc_t rl = make_rsrc(meta, meta_bytes);
+    ls = __builtin_amdgcn_raw_buffer_load_b128(
+        rl, (int)threadIdx.x < lpieces ? (T0 * 16 * F::tab_dw / 4 + (int)threadIdx.x) * 16 : (int)kOutOfRange, 0,
+        kNonTemporal);
+  }
+  // x: LDS piece i (16 bytes) is (j, n) = (i / NB, i % NB); columns past K read as 0.
+  const int xpieces = Kp / 8 * NB;  // a multiple of 64
+  for (int i = w; 64 * i < xpieces; i += kWaves) {
+    const int piece = 64 * i + lane;
+    const int j = piece / NB, n = piece % NB;
+    const int off = 8 * j < K ? (n * K + 8 * j) * 2 : (int)kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xs + 512 * i), 16, off, 0,
+                                             0, 0);
+  }
+  const int E0 = __builtin_amdgcn_readlane(ev, 0), E1 = __builtin_amdgcn_readlane(ev, 1);
+  const int A0 = E0 & ~3;  // entries [A0, Acap) of the workgroup's run are copied into LDS
+  const int Acap = min(E1, A0 + ent_cap);
+  {
+    const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
+    const int pieces = (Acap - A0 + 3) >> 2;
+    for (int i = w; 64 * i < pieces; i += kWaves) {
+      const int piece = 64 * i + lane;
+      if (piece < pieces)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(ent_lds + 256 * i), 16,
+                                                 (A0 + 4 * piece) * 4, 0, 0, kNonTemporal);
+    }
+  }
+
+  const uint32_t voff = (uint32_t)lane * 4 * BITS;
+  const uint32_t zoff = (uint32_t)(lane & 15) * 16 + (uint32_t)(lane >> 4) * 4;
+  const uint32_t spoff = 256 + (uint32_t)(lane >> 4) * 64 + (uint32_t)(lane & 15) * 4;
+  uint32_t cb[R][BITS];
+  uint32_t sb[R][2];
+  auto issue = [&](int u, int b) {  // b: block of the workgroup, -1 for none
+    const bool in = b >= 0;
+    const uint32_t g = (uint32_t)(T0 * nkb + b);
+    load_chunk<BITS>(cb[u], rc, in ? g * BB + voff : kOutOfRange);
+    if constexpr (!F::lut) {
+      sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? g * 512 + zoff : kOutOfRange), 0, kNonTemporal);
+      sb[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? g * 512 + spoff : kOutOfRange), 0, kNonTemporal);
+    } else {
+      sb[u][0] = sb[u][1] = 0;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < R; ++u) issue(u, b0 + u < b1 ? b0 + u : -1);
+
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
+  if constexpr (F::lut) {
+    if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
+  }
+  if (threadIdx.x < kWaves) {  // tiles touched by each wave's run: [first, last], empty if first > last
+    const int v = threadIdx.x;
+    const int c0 = v * L / kWaves, c1 = (v + 1) * L / kWaves;
+    runs[2 * v] = c1 > c0 ? c0 / nkb : 1;
+    runs[2 * v + 1] = c1 > c0 ? (c1 - 1) / nkb : 0;
+  }
+  if (threadIdx.x == 0) *group_ctr = 0;
+  __syncthreads();
+
+  // The stream: this wave's run, tile by tile.
+  int tl = b0 / nkb, kb = b0 - tl * nkb;  // local tile and K-block of the next block
+  uint32_t tab[F::tab_dw];
+  auto planes = [&]() {
+    if constexpr (F::lut) {
+      const uint32_t* Lt = lut_lds + (tl * 16 + (lane & 15)) * F::tab_dw;
+      uint32_t Lr[F::tab_dw];
+#pragma unroll
+      for (int i = 0; i < F::tab_dw; ++i) Lr[i] = Lt[i];
+      if constexpr (BITS == 4) l4_planes(Lr, tab);
+      else l3_planes(Lr, tab);
+    } else {
+      tab[0] = 0;
+    }
+  };
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto flush = [&]() {  // acc[i]: row 4*(lane/16) + i of local tile tl, batch column lane % 16
+    float* d = slots + (w + tl) * 16 * NB;
+    if ((lane & 15) < NB)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[(4 * (lane >> 4) + i) * NB + (lane & 15)] = acc[i];
+  };
+  if (b0 < b1) planes();
+  const uint16_t* xb = xs + (4 * (lane >> 4) * NB + ((lane & 15) & (NB - 1))) * 8;
+  for (int bb = b0; bb < b1; bb += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const bool live = bb + u < b1;
+      if (live) {
+        if (kb == nkb) {
+          flush();
+          acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+          ++tl;
+          kb = 0;
+          planes();
+        }
+        uint32_t am[F::n_mfma][4];
+        if constexpr (F::lut) {
+          decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
+        } else {
+          const uint32_t st[2] = {perm(sb[u][0], sb[u][1], 0x05040100u), perm(sb[u][0], sb[u][1], 0x07060302u)};
+          decode_chunk<FMT, BITS>(cb[u], st, tab, am);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const half8_t bx = *(const half8_t*)(xb + (16 * kb + s2) * NB * 8);
+          acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
+          if constexpr (!F::lut) acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
+        }
+        ++kb;
+      }
+      // Unconditional, so that every slot has the same loads behind it and
+      // the waits stay per slot (a load past the run is out of range).
+      issue(u, bb + u + R < b1 ? bb + u + R : -1);
+    }
+  }
+  if (b0 < b1) flush();
+
+  // Outliers, before the barrier: the waves that finish their runs first
+  // (the arbiter favours older waves) take groups of four CSR rows from an
+  // LDS counter.  Each DPP row of 16 lanes takes one CSR row; a lane takes
+  // every 16th outlier of its row, reads the NB activations of the outlier's
+  // column from xs and keeps NB partial sums, which four DPP steps add up
+  // across the 16 lanes.  A row's sum is the same whichever wave takes it.
+  {
+    const int sl = lane & 15, rq = lane >> 4;
+    for (;;) {
+      int g = 0;
+      if (lane == 0) g = lds_fetch_add(group_ctr, 1);
+      g = __builtin_amdgcn_readfirstlane(g);
+      if (4 * g >= nrows) break;
+      const int r = 4 * g + rq;
+      const bool real = r < nrows;
+      const int p0 = real ? rp_lds[r] : 0, p1 = real ? rp_lds[r + 1] : 0;
+      const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
+      float an[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) an[j] = 0.f;
+      auto term = [&](uint32_t e) {
+        const int c = (int)(e & 0xFFFFu);
+        const uint16_t* xc = xs + (c >> 3) * NB * 8 + (c & 7);
+        const uint32_t vlo = e >> 16, vhi = e & 0xFFFF0000u;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          const uint32_t pr = (uint32_t)xc[16 * j] | ((uint32_t)xc[16 * j + 8] << 16);
+          an[2 * j] = dot2(vlo, pr, an[2 * j]);
+          an[2 * j + 1] = dot2(vhi, pr, an[2 * j + 1]);
+        }
+      };
+      for (int p = p0 + sl; p < pm; p += 16) term(ent_lds[p - A0]);
+      int p = max(p0, Acap) + sl;
+      for (; p + 48 < p1; p += 64) {  // four outliers from HBM in flight
+        uint32_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = entries[p + 16 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) term(e[u]);
+      }
+      for (; p < p1; p += 16) term(entries[p]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        float v = an[j];
+        v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+        v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+        v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror
+        v += dpp_mov<0x140, 0xF>(v);  // row_mirror: every lane of the row holds the sum
+        an[j] = v;
+      }
+      if (real && sl == 0)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) csr[r * NB + j] = an[j];
+    }
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
-    const int r = i / NB, n = i % NB;
-    const float* pr = part + (r >> 4) * CPT * 16 * NB + (r & 15) * NB + n;
+    const int r = i / NB, n = i % NB, t = r >> 4;
     float v = 0.f;
-    for (int j = 0; j < CPT; ++j) v += pr[j * 16 * NB];
-    if constexpr (B1) y[T0 * 16 + r] = v + csr[r];
-    else y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
+    for (int u = 0; u < kWaves; ++u)
+      if (runs[2 * u] <= t && t <= runs[2 * u + 1]) v += slots[((u + t) * 16 + (r & 15)) * NB + n];
+    y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
   }
 }
 
@@ -734,11 +1039,11 @@ constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kEntCapBytes = 64 * 1024;  // CSR entries staged per workgroup, at most
 constexpr size_t kOneWorkgroupLds = kLdsBytes / 2 + 1024;
 
-// LDS per tile of a workgroup: chunk partials, CSR sums, row_ptr entries, table.
+// LDS per tile of a workgroup: chunk partials, CSR sums (batch NB), row_ptr entries, table.
 size_t stream_lds_per_tile(const BlobHeader& h, int nb, int pf) {
   const size_t cpt = (size_t)((h.nkb + pf - 1) / pf);
   const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
-  return cpt * 16 * nb * 4 + 16 * (size_t)nb * 4 + 16 * 4 + 16 * tab;
+  return cpt * 16 * nb * 4 + (nb == 1 ? 0 : 16 * (size_t)nb * 4) + 16 * 4 + 16 * tab;
 }
 
 // One workgroup per CU, more when the per-tile LDS of 256 workgroups would
@@ -805,11 +1110,55 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
   return hipGetLastError();
 }
 
+// LDS of the x-resident batched kernel apart from the CSR entries: x, partial
+// slots, CSR sums, row_ptr slice, run table and CSR group count, tables.
+size_t xlds_fixed(const BlobHeader& h, int grid, int nb) {
+  const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
+  const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
+  return (size_t)h.Kp * nb * 2 + (tw + 15) * 16 * nb * 4 + tw * 16 * nb * 4 + ((tw * 16 + 4) & ~(size_t)3) * 4 +
+         (2 * kWaves + 4) * 4 + tw * 16 * tab;
+}
+
+// One workgroup per CU, more when a workgroup would get over 32 tiles (the
+// row_ptr slice is staged by one thread per row).
+int xlds_grid(const BlobHeader& h) {
+  const int g = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
+  const int need = (h.tiles + 31) / 32;
+  return g > need ? g : need;
+}
+
+// The x-resident kernel runs when x and the partials leave at least 1 KiB of LDS.
+bool xlds_fits(const BlobHeader& h, int nb) { return xlds_fixed(h, xlds_grid(h), nb) + 1024 <= kLdsBytes; }
+
+template <int FMT, int BITS, int NB>
+hipError_t launch_xlds(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+  constexpr int R = 4;  // code ring slots per wave
+  const BlobHeader& h = p->h;
+  const int grid = xlds_grid(h);
+  const size_t fixed = xlds_fixed(h, grid, NB);
+  size_t cap = kLdsBytes - fixed;  // CSR entries staged in LDS
+  if (cap > kEntCapBytes) cap = kEntCapBytes;
+  cap &= ~(size_t)1023;  // whole 1 KiB wave copies
+  size_t lds = fixed + cap;
+  if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_xlds<FMT, BITS, NB, R>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
+  const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
+  hipLaunchKernelGGL((k_xlds<FMT, BITS, NB, R>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
+                     (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
+                     (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
+                     meta_bytes, (int)h.nnz, (int)(cap / 4));
+  return hipGetLastError();
+}
+
 template <int FMT, int BITS>
 hipError_t launch_run(const qgemv_plan* p, const uint16_t* x, float* y, int batch, hipStream_t st) {
   if (batch == 1) return launch_stream<FMT, BITS, 1>(p, x, y, st);
-  if (batch == 8) return launch_stream<FMT, BITS, 8>(p, x, y, st);
-  return launch_stream<FMT, BITS, 16>(p, x, y, st);
+  if (batch == 8)
+    return xlds_fits(p->h, 8) ? launch_xlds<FMT, BITS, 8>(p, x, y, st) : launch_stream<FMT, BITS, 8>(p, x, y, st);
+  return xlds_fits(p->h, 16) ? launch_xlds<FMT, BITS, 16>(p, x, y, st) : launch_stream<FMT, BITS, 16>(p, x, y, st);
 }
 
 template <int FMT, int BITS>
