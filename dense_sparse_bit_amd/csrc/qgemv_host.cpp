@@ -306,6 +306,23 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
   uint32_t* ent = (uint32_t*)(blob + h.off_entries);
   for (int64_t p = 0; p < w->nnz; ++p)
     ent[p] = (uint32_t)w->col_idx[p] | ((uint32_t)w->values[p] << 16);
+
+  // The outliers again, grouped by (tile, K-block): a counting sort over the
+  // rows in order keeps rows, then columns, ascending inside each group.
+  const size_t nblocks = (size_t)h.tiles * nkb;
+  int32_t* boff = (int32_t*)(blob + h.off_boff);
+  uint32_t* bent = (uint32_t*)(blob + h.off_bent);
+  for (int row = 0; row < M; ++row)
+    for (int32_t p = w->row_ptr[row]; p < w->row_ptr[row + 1]; ++p)
+      ++boff[(size_t)(row / kTileRows) * nkb + w->col_idx[p] / kBlockK + 1];
+  for (size_t i = 0; i < nblocks; ++i) boff[i + 1] += boff[i];
+  std::vector<int32_t> fill(boff, boff + nblocks);
+  for (int row = 0; row < M; ++row)
+    for (int32_t p = w->row_ptr[row]; p < w->row_ptr[row + 1]; ++p) {
+      const int c = w->col_idx[p];
+      const size_t i = (size_t)(row / kTileRows) * nkb + c / kBlockK;
+      bent[fill[i]++] = (uint32_t)(c % kBlockK) | ((uint32_t)(row % kTileRows) << 7) | ((uint32_t)w->values[p] << 16);
+    }
   return QGEMV_OK;
 }
 

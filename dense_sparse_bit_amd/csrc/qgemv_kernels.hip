@@ -263,17 +263,20 @@ __device__ __forceinline__ void lds_barrier() {
 //
 // Batch 1 (NB = 1): x sits in LDS and every lane reads its B operand from
 // there (the same x in all 16 MFMA columns).  The outliers of the
-// workgroup's rows are one contiguous run of CSR entries; right after the
-// prologue barrier the waves copy that run (up to the LDS space left) from HBM
-// straight into LDS with buffer-to-LDS loads, which land while the dense
-// stream runs.  After the stream each wave sums the outliers of its rows from
-// LDS.
+// workgroup's rows are one contiguous run of CSR entries; after its first
+// chunk each wave copies its share of that run (up to the LDS space left)
+// from HBM straight into LDS with buffer-to-LDS loads, which land while the
+// dense stream runs.  After the stream 16 lanes per row add the row's
+// outliers and its chunk partials.
 //
-// Batch 8 / 16 (NB = batch): column n of the MFMA is batch row n.  x is
-// 2 KiB or 4 KiB per K-block and comes from L2 through the ring, next to the
-// codes of the same K-block; partials are kept per batch column.  The CSR run
-// is staged in LDS the same way; after the stream x is staged transposed in
-// LDS, KC columns per pass, and each outlier meets all batch rows at once.
+// Batch 8 / 16 (NB = batch), used when x does not fit in LDS: column n of the
+// MFMA is batch row n.  x is 2 KiB or 4 KiB per K-block and comes from L2
+// through the ring, next to the codes of the same K-block; partials are kept
+// per batch column.  The outliers go through the MFMAs too: the ring also
+// loads the outliers of each block (grouped by block in the blob), the wave
+// scatters them into its own zeroed 16x128 FP16 tile in LDS, reads the tile
+// back as four A operands and multiplies them with the block's x already in
+// registers, then clears what it wrote.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 16;
 constexpr uint32_t kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), no wait on the other counters
@@ -281,12 +284,14 @@ constexpr uint32_t kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), no wait on the o
 template <int FMT, int BITS, int CH, int NR, int NB>
 __global__ void __launch_bounds__(64 * kWaves)
 k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
-         const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
-         int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap, int KC) {
+         const uint32_t* __restrict__ entries, const int32_t* __restrict__ boff, const uint32_t* __restrict__ bent,
+         const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K, int Kp, int nkb, int tiles,
+         uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap) {
   using F = Fmt<FMT, BITS>;
   constexpr int BB = 256 * BITS;
   constexpr bool B1 = NB == 1;
   constexpr int PF = CH * NR;  // ring slots: NR chunks of CH K-blocks in flight per wave
+  static_assert(B1 || NR == 1, "batch NB keeps one chunk in flight");
   extern __shared__ uint32_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -323,15 +328,16 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   };
   const int nrows = min(TW * 16, M - T0 * 16);  // real rows of the workgroup
 
-  // LDS: x [Kp+8] fp16 (batch 1 only) | part [TW*CPT][16][NB] | csr [TW*16][NB] (batch NB only) | row_ptr [TW*16+4]
-  //      | LUT [TW*16][tab_dw] | CSR entries [ent_cap] | x transposed [KC+1][NB/2] FP16 pairs (batch NB only)
+  // LDS, batch 1:  x [Kp+8] fp16 | part [TW*CPT][16] | row_ptr [TW*16+4] | LUT [TW*16][tab_dw] | CSR entries [ent_cap]
+  //      batch NB: part [TW*CPT][16][NB] | block offsets [TW*nkb+1, padded] | LUT | outlier tiles [16 waves][16][128] FP16
+  // (the counters sit in spare slots at the end of the row_ptr / offsets region)
   uint16_t* x_lds = (uint16_t*)lds;  // batch 1: x, then 16 zero bytes
   float* part = (float*)(lds + (B1 ? Kp / 2 + 4 : 0));
-  float* csr = part + nchunks * 16 * NB;  // batch NB only
-  int* rp_lds = (int*)(csr + (B1 ? 0 : TW * 16 * NB));
-  uint32_t* lut_lds = (uint32_t*)(rp_lds + TW * 16 + 4);  // 16-byte aligned
-  uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);
-  uint32_t* xT = ent_lds + ent_cap;
+  int* rp_lds = (int*)(part + nchunks * 16 * NB);
+  const int rp_n = B1 ? TW * 16 + 4 : ((TW * nkb + 6) & ~3);
+  uint32_t* lut_lds = (uint32_t*)(rp_lds + rp_n);  // 16-byte aligned
+  uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);  // batch 1
+  uint16_t* otile = (uint16_t*)ent_lds + 2048 * w;  // batch NB: this wave's outlier tile, A-operand order
 
   const rsrc_t rc = make_rsrc(codes, codes_bytes);
   const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
@@ -369,13 +375,25 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
     }
   }
   const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
-  const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
-                                               rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
-                                         : 0;
+  const int rpn = B1 && threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
+                                               : 0;
   // The bounds [E0, E1) of the workgroup's outliers, in lanes 0 and 1 of
   // every wave: vector loads, which the LDS barrier below does not wait for
   // (scalar loads would hold it until they return).
-  const int ev = lane < 2 ? __builtin_amdgcn_raw_buffer_load_b32(rr, (T0 * 16 + (lane ? nrows : 0)) * 4, 0, 0) : 0;
+  const int ev = B1 && lane < 2 ? __builtin_amdgcn_raw_buffer_load_b32(rr, (T0 * 16 + (lane ? nrows : 0)) * 4, 0, 0)
+                                : 0;
+  // Batch NB: the outlier offsets of the workgroup's blocks, for LDS (at most
+  // 4 per thread; the host keeps TW * nkb below 4096).
+  const rsrc_t rbo = make_rsrc(boff, (uint32_t)((uint64_t)tiles * nkb + 1) * 4);
+  int bo[4] = {0, 0, 0, 0};
+  if constexpr (!B1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = (int)threadIdx.x + 1024 * k;
+      bo[k] = __builtin_amdgcn_raw_buffer_load_b32(rbo, i <= TW * nkb ? (T0 * nkb + i) * 4 : (int)kOutOfRange, 0, 0);
+    }
+  }
   u32x4_t ls = {0u, 0u, 0u, 0u};
   const int lpieces = F::lut ? TW * 16 * F::tab_dw / 4 : 0;  // 16-byte pieces of the tables
   if constexpr (F::lut) {
@@ -387,6 +405,18 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   uint32_t cb[PF][BITS];
   uint32_t sb[PF][SBW];
   u32x4_t xr[B1 ? 1 : PF][4];
+  // Batch NB: the outliers of each ring slot's block, one per lane (up to 64;
+  // more are read when the block is decoded), and their first index and count.
+  uint32_t ent[B1 ? 1 : PF];
+  int elo[B1 ? 1 : PF], ecnt[B1 ? 1 : PF];
+  const rsrc_t rbe = make_rsrc(bent, (uint32_t)nnz * 4);
+  auto issue_ent = [&](int u, int lo, int n) {
+    if constexpr (!B1) {
+      ent[u] = __builtin_amdgcn_raw_buffer_load_b32(rbe, lane < n ? (lo + lane) * 4 : (int)kOutOfRange, 0, kNonTemporal);
+      elo[u] = lo;
+      ecnt[u] = n;
+    }
+  };
   auto issue = [&](int u, int g) {  // g: blob block index, -1 for none
     const bool in = g >= 0;
     load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
@@ -431,16 +461,38 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
     if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
   }
   for (int j = threadIdx.x; j < nchunks * 16 * NB; j += kThreads) part[j] = 0.f;  // chunks past a short tile end
-  int* chunk_ctr = rp_lds + TW * 16 + 2;  // a spare slot after the row_ptr slice
+  if constexpr (!B1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = (int)threadIdx.x + 1024 * k;
+      if (i <= TW * nkb) rp_lds[i] = bo[k];
+    }
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ((u32x4_t*)otile)[lane + 64 * k] = z;
+  }
+  int* chunk_ctr = rp_lds + rp_n - 2;  // a spare slot after the row_ptr slice / block offsets
   if (threadIdx.x == 0) *chunk_ctr = kWaves;
   lds_barrier();
+  // Batch NB: the outlier offsets of a chunk's blocks (lane i: block i's start, i <= nv).
+  auto chunk_offsets = [&](const Chunk& k) {
+    return lane <= k.nv && k.nv > 0 ? rp_lds[k.g0 - T0 * nkb + lane] : 0;
+  };
+  if constexpr (!B1) {
+    const int obv = chunk_offsets(ck[0]);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int lo = __builtin_amdgcn_readlane(obv, u);
+      issue_ent(u, lo, u < ck[0].nv ? __builtin_amdgcn_readlane(obv, u + 1) - lo : 0);
+    }
+  }
 
-  // Set-up the dense stream does not need, done by each wave after its first
-  // chunk (or after the stream if it had none), when the row_ptr values have
-  // long arrived: the row_ptr slice goes to LDS, and the CSR entries
-  // [A0, A0 + ent_cap) of the workgroup's run are copied from HBM straight
-  // into LDS, 1 KiB per wave instruction (16 bytes per lane).  Both are first
-  // read after the barrier that ends the stream.
+  // Batch 1: set-up the dense stream does not need, done by each wave after
+  // its first chunk (or after the stream if it had none), when the row_ptr
+  // values have long arrived: the row_ptr slice goes to LDS, and the CSR
+  // entries [A0, A0 + ent_cap) of the workgroup's run are copied from HBM
+  // straight into LDS, 1 KiB per wave instruction (16 bytes per lane).  Both
+  // are first read after the barrier that ends the stream.
   int A0 = 0, Acap = 0;
   bool late_done = false;
   auto late_setup = [&]() {
@@ -496,6 +548,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
     for (int r = 0; r < NR; ++r) {
       const Chunk cur = ck[r];
       const Chunk nx = next_chunk();
+      const int obv = B1 ? 0 : chunk_offsets(nx);
       const bool live = cur.q < nchunks;
       if (live && T0 + cur.t != tc) {
         tc = T0 + cur.t;
@@ -544,9 +597,48 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
               if constexpr (!F::lut)
                 acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
             }
+            if constexpr (!B1) {
+              // The block's outliers: scattered into the wave's (zero) 16x128
+              // tile in A-operand order, read back as four A operands and
+              // multiplied with the block's x like the dense codes, then
+              // cleared again.
+              const int n = ecnt[sl];
+              if (n > 0) {
+                auto place = [&](uint32_t e) {
+                  const uint32_t c = e & 127u, m = (e >> 7) & 15u;
+                  return (((c >> 3) & 3u) * 64u + m + 16u * (c >> 5)) * 8u + (c & 7u);
+                };
+                uint32_t oa = 0;
+                if (lane < n) {
+                  oa = place(ent[sl]);
+                  otile[oa] = (uint16_t)(ent[sl] >> 16);
+                }
+                for (int p = 64; p < n; p += 64)  // more than 64 in the block
+                  if (lane + p < n) {
+                    const uint32_t e = bent[elo[sl] + p + lane];
+                    otile[place(e)] = (uint16_t)(e >> 16);
+                  }
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                  const u32x4_t a = ((const u32x4_t*)otile)[s2 * 64 + lane];
+                  acc = mfma(h8(a[0], a[1], a[2], a[3]), __builtin_bit_cast(half8_t, xr[sl][s2]), acc);
+                }
+                if (n <= 64) {
+                  if (lane < n) otile[oa] = 0;
+                } else {
+                  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                  for (int k = 0; k < 4; ++k) ((u32x4_t*)otile)[lane + 64 * k] = z;
+                }
+              }
+            }
           }
         }
         issue(sl, u < nx.nv ? nx.g0 + u : -1);
+        if constexpr (!B1) {
+          const int lo = __builtin_amdgcn_readlane(obv, u);
+          issue_ent(sl, lo, u < nx.nv ? __builtin_amdgcn_readlane(obv, u + 1) - lo : 0);
+        }
       }
       if constexpr (UG1) {  // add the 8 groups (lanes 16j + 0..7) of every row
 #pragma unroll
@@ -573,9 +665,13 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       }
       ck[r] = nx;
     }
+    if constexpr (B1) {
+      if (!late_done) late_setup();
+    }
+  }
+  if constexpr (B1) {
     if (!late_done) late_setup();
   }
-  if (!late_done) late_setup();
 
   // Outliers: entries of the LDS run come from LDS, any beyond it from HBM.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -620,93 +716,12 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
       if (r < nrows && sl == 0) y[T0 * 16 + r] = v;
     }
   } else {
-    // x is staged transposed, KC columns per pass (plus one zero column), so
-    // that the NB activations of one column are NB*2 contiguous bytes.  Each
-    // DPP row of 16 lanes takes one CSR row (four rows per wave at a time); a
-    // lane takes every 16th entry of its row, reads the entry's NB
-    // activations with 16-byte LDS loads and keeps NB partial sums, which four
-    // DPP steps add up across the 16 lanes.
-    constexpr int NP = NB / 2;
-    const int sl = lane & 15, rr = lane >> 4;
-    for (int c0 = 0; c0 < K; c0 += KC) {
-      const int kc = min(KC, K - c0);
-      if (c0) __syncthreads();
-      // piece i = (k8, pair): 8 columns of batch rows 2 pair and 2 pair + 1, stored as 8 FP16 pairs
-      const int npieces = (kc / 8) * NP;
-      for (int i0 = threadIdx.x; i0 < npieces; i0 += 4 * 64 * kWaves) {
-        u32x4_t lo[4], hi[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 64 * kWaves;
-          const int pr = i % NP, k8 = i / NP;
-          const int off = i < npieces ? ((2 * pr) * K + c0 + 8 * k8) * 2 : (int)kOutOfRange;
-          lo[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-          hi[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, off == (int)kOutOfRange ? off : off + K * 2, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 64 * kWaves;
-          if (i < npieces) {
-            uint32_t* d = xT + 8 * (i / NP) * NP + i % NP;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              d[(2 * j) * NP] = perm(hi[u][j], lo[u][j], 0x05040100u);
-              d[(2 * j + 1) * NP] = perm(hi[u][j], lo[u][j], 0x07060302u);
-            }
-          }
-        }
-      }
-      if (threadIdx.x < NP) xT[kc * NP + threadIdx.x] = 0u;  // the zero column
-      __syncthreads();
-      for (int j0 = 0; w + 16 * j0 < nrows; j0 += 4) {
-        const int r = w + 16 * (j0 + rr);  // this DPP row's CSR row (may be past the end)
-        const bool real = r < nrows;
-        const int p0 = real ? rp_lds[r] : 0, p1 = real ? rp_lds[r + 1] : 0;
-        const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
-        float an[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) an[j] = 0.f;
-        auto term = [&](uint32_t e) {
-          const int col = (int)(e & 0xFFFFu) - c0;
-          const int c = col >= 0 && col < kc ? col : kc;  // out of this pass: the zero column
-          const uint32_t vlo = e >> 16, vhi = e & 0xFFFF0000u;
-#pragma unroll
-          for (int h = 0; h < NB / 8; ++h) {
-            const u32x4_t xv = *(const u32x4_t*)(xT + c * NP + 4 * h);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              an[8 * h + 2 * j] = dot2(vlo, xv[j], an[8 * h + 2 * j]);
-              an[8 * h + 2 * j + 1] = dot2(vhi, xv[j], an[8 * h + 2 * j + 1]);
-            }
-          }
-        };
-        for (int p = p0 + sl; p < pm; p += 16) term(ent_lds[p - A0]);
-        for (int p = max(p0, Acap) + sl; p < p1; p += 16) term(entries[p]);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          float v = an[j];
-          v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-          v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-          v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror
-          v += dpp_mov<0x140, 0xF>(v);  // row_mirror: every lane of the row holds the sum
-          an[j] = v;
-        }
-        if (real && sl == 0) {
-          float* d = csr + r * NB;
-#pragma unroll
-          for (int j = 0; j < NB; ++j) d[j] = (c0 ? d[j] : 0.f) + an[j];
-        }
-      }
-    }
-  }
-  if constexpr (!B1) {
-    __syncthreads();
     for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
       const int r = i / NB, n = i % NB;
       const float* pr = part + (r >> 4) * CPT * 16 * NB + (r & 15) * NB + n;
       float v = 0.f;
       for (int j = 0; j < CPT; ++j) v += pr[j * 16 * NB];
-      y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
+      y[(size_t)n * M + T0 * 16 + r] = v;
     }
   }
 }
@@ -1039,32 +1054,38 @@ constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kEntCapBytes = 64 * 1024;  // CSR entries staged per workgroup, at most
 constexpr size_t kOneWorkgroupLds = kLdsBytes / 2 + 1024;
 
-// LDS per tile of a workgroup: chunk partials, CSR sums (batch NB), row_ptr entries, table.
-size_t stream_lds_per_tile(const BlobHeader& h, int nb, int pf) {
-  const size_t cpt = (size_t)((h.nkb + pf - 1) / pf);
+// LDS per tile of a workgroup.  Batch 1: chunk partials, row_ptr entries,
+// table.  Batch NB: chunk partials, block outlier offsets, table.
+size_t stream_lds_per_tile(const BlobHeader& h, int nb, int ch) {
+  const size_t cpt = (size_t)((h.nkb + ch - 1) / ch);
   const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;
-  return cpt * 16 * nb * 4 + (nb == 1 ? 0 : 16 * (size_t)nb * 4) + 16 * 4 + 16 * tab;
+  return nb == 1 ? cpt * 16 * 4 + 16 * 4 + 16 * tab : cpt * 16 * nb * 4 + (size_t)h.nkb * 4 + 16 * tab;
+}
+
+// LDS besides the per-tile parts and the CSR entries: batch 1, x with 16 zero
+// bytes and the spare row_ptr slots; batch NB, offset padding and the 16
+// waves' 4 KiB outlier tiles.
+size_t stream_lds_extra(const BlobHeader& h, int nb) {
+  return nb == 1 ? (size_t)h.Kp * 2 + 16 + 16 : 32 + (size_t)kWaves * 4096;
 }
 
 // One workgroup per CU, more when the per-tile LDS of 256 workgroups would
-// not fit.  Batch 1 keeps at least 16 KiB for CSR entries; batch NB keeps at
-// least 64 KiB for CSR entries and transposed x.
-int stream_grid(const BlobHeader& h, int nb, int pf) {
-  const size_t x = nb == 1 ? (size_t)h.Kp * 2 + 16 : 0;
-  const size_t keep = nb == 1 ? 16 * 1024 : 64 * 1024;
-  size_t max_tw = (kLdsBytes - x - keep - 16) / stream_lds_per_tile(h, nb, pf);
+// not fit (batch 1 keeps at least 16 KiB for CSR entries) or, for batch NB,
+// a workgroup's block offsets would exceed 4096.
+int stream_grid(const BlobHeader& h, int nb, int ch) {
+  const size_t keep = nb == 1 ? 16 * 1024 : 0;
+  size_t max_tw = (kLdsBytes - stream_lds_extra(h, nb) - keep) / stream_lds_per_tile(h, nb, ch);
   if (max_tw > 32) max_tw = 32;
+  if (nb > 1 && max_tw > (size_t)(4095 / h.nkb)) max_tw = (size_t)(4095 / h.nkb);
   if (max_tw < 1) max_tw = 1;
   int g = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
   const int need = (int)((h.tiles + max_tw - 1) / max_tw);
   return g > need ? g : need;
 }
 
-// LDS of x (batch 1), partials, CSR sums, row_ptr slice and tables.
-size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int pf) {
+size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int ch) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-  const size_t x = nb == 1 ? (size_t)h.Kp * 2 + 16 : 0;  // x and 16 zero bytes
-  return x + tw * stream_lds_per_tile(h, nb, pf) + 16;  // + the 4 spare row_ptr slots
+  return stream_lds_extra(h, nb) + tw * stream_lds_per_tile(h, nb, ch);
 }
 
 template <int FMT, int BITS, int NB>
@@ -1074,27 +1095,15 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
   const BlobHeader& h = p->h;
   const int grid = stream_grid(h, NB, CH);
   const size_t fixed = stream_lds_fixed(h, grid, NB, CH);
-  // The rest of LDS: batch 1 gives it to CSR entries; batch NB gives the
-  // entries about 1.5x a workgroup's average share and the remainder to the
-  // transposed x of one pass (KC columns, a multiple of 32).
-  const size_t rest = kLdsBytes - fixed;
-  size_t cap = rest;
-  int KC = 0;
-  if (NB > 1) {
-    const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-    const size_t avg = (size_t)((double)h.nnz * (double)(tw * 16) / (double)h.M * 4.0);
-    cap = avg + avg / 2 + 1023;
-    const size_t most = rest - 33 * NB * 2;  // leave room for one pass of 32 columns and the zero column
-    if (cap > most) cap = most;
+  if (fixed > kLdsBytes) return hipErrorInvalidValue;
+  // Batch 1 gives the rest of LDS (up to 64 KiB) to the CSR entries.
+  size_t cap = 0;
+  if (NB == 1) {
+    cap = kLdsBytes - fixed;
+    if (cap > kEntCapBytes) cap = kEntCapBytes;
+    cap &= ~(size_t)1023;  // whole 1 KiB wave loads
   }
-  if (cap > kEntCapBytes) cap = kEntCapBytes;
-  cap &= ~(size_t)1023;  // whole 1 KiB wave loads
-  if (NB > 1) {
-    KC = (int)((rest - cap) / (NB * 2) - 1) & ~31;
-    if (KC > h.K) KC = h.K;
-    if (KC < 32) return hipErrorInvalidValue;
-  }
-  size_t lds = fixed + cap + (NB > 1 ? (size_t)(KC + 1) * NB * 2 : 0);
+  size_t lds = fixed + cap;
   // More than half of LDS keeps a second workgroup off the CU: one per CU.
   if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
   // once per instantiation (thread-safe static initialisation)
@@ -1105,8 +1114,9 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
   hipLaunchKernelGGL((k_stream<FMT, BITS, CH, NR, NB>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
-                     (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
-                     meta_bytes, (int)h.nnz, (int)(cap / 4), KC);
+                     (const uint32_t*)(p->blob + h.off_entries), (const int32_t*)(p->blob + h.off_boff),
+                     (const uint32_t*)(p->blob + h.off_bent), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
+                     meta_bytes, (int)h.nnz, (int)(cap / 4));
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // qgemv_layout.h -- the gfx950 blob written by qgemv_repack and read by the kernels.
 //
-// Blob = header | codes | meta | row_ptr | entries, every section 256-byte aligned.
+// Blob = header | codes | meta | row_ptr | entries | boff | bent, every
+// section 256-byte aligned.
 //
 // Tiles.  Rows are grouped in tiles of 16 (the M side of a 16x16x32 MFMA);
 // K is padded to Kp, a multiple of 128, and cut into K-blocks of 128 codes
@@ -44,6 +45,12 @@
 //         16-byte piece of the s plane.
 // row_ptr int32 [M+1] (as given).
 // entries uint32 [nnz]: column (low 16 bits) | FP16 value bits (high 16 bits).
+// boff    int32 [tiles * nkb + 1]: the outliers of (tile, K-block) index i =
+//         t * nkb + b are bent[boff[i] .. boff[i+1]).
+// bent    uint32 [nnz]: the same outliers grouped by (tile, K-block), rows
+//         and then columns ascending inside a group: column inside the
+//         K-block (bits 0-6) | row inside the tile (bits 7-10) | FP16 value
+//         bits (16-31).
 #pragma once
 
 #include <stdint.h>
@@ -51,7 +58,7 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 3;
+constexpr uint32_t kVersion = 4;
 constexpr int kTileRows = 16;
 constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
@@ -69,6 +76,7 @@ struct BlobHeader {
   uint32_t meta_unit_bytes;  // LUT: bytes per row; UNIFORM: bytes per (tile, K-block)
   int32_t Kp;                // K padded to a multiple of kBlockK
   int32_t nkb;               // Kp / kBlockK
+  uint64_t off_boff, off_bent;  // outliers grouped by (tile, K-block)
 };
 static_assert(sizeof(BlobHeader) <= kHeaderBytes, "header too large");
 
@@ -98,7 +106,9 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
   h.off_meta = align_up(h.off_codes + nblocks * h.block_bytes);
   h.off_rowptr = align_up(h.off_meta + meta_bytes);
   h.off_entries = align_up(h.off_rowptr + 4ull * ((uint64_t)M + 1));
-  h.total_bytes = align_up(h.off_entries + 4ull * (uint64_t)nnz);
+  h.off_boff = align_up(h.off_entries + 4ull * (uint64_t)nnz);
+  h.off_bent = align_up(h.off_boff + 4ull * (nblocks + 1));
+  h.total_bytes = align_up(h.off_bent + 4ull * (uint64_t)nnz);
   return h;
 }
 

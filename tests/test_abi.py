@@ -92,6 +92,26 @@ def test_repack_roundtrip_oracle_encoding(name, M, K):
     ent = blob[off_entries:off_entries + 4 * nnz].view(np.uint32)
     assert np.array_equal(ent & 0xFFFF, enc["col_idx"])
     assert np.array_equal((ent >> 16).astype(np.uint16), enc["values"].view(np.uint16))
+    _check_block_outliers(blob, enc, M, K)
+
+
+def _check_block_outliers(blob, w, M, K):
+    """The outliers grouped by (tile, K-block) are the CSR outliers, each once, in row-then-column order."""
+    off = blob[:256].view(np.uint64)
+    off_boff, off_bent = int(off[12]), int(off[13])
+    tiles, nkb = (M + 15) // 16, (K + 127) // 128
+    nnz = int(w["row_ptr"][-1])
+    boff = blob[off_boff:off_boff + 4 * (tiles * nkb + 1)].view(np.int32)
+    bent = blob[off_bent:off_bent + 4 * nnz].view(np.uint32)
+    assert boff[0] == 0 and boff[-1] == nnz and np.all(np.diff(boff) >= 0)
+    rows = np.repeat(np.arange(M), np.diff(w["row_ptr"]))
+    cols = np.asarray(w["col_idx"], dtype=np.int64)
+    vals = np.asarray(w["values"]).view(np.uint16)
+    blk = (rows // 16) * nkb + cols // 128
+    order = np.lexsort((cols, rows, blk))
+    assert np.array_equal(np.bincount(blk, minlength=tiles * nkb), np.diff(boff))
+    exp = (cols[order] % 128) | ((rows[order] % 16) << 7) | (vals[order].astype(np.int64) << 16)
+    assert np.array_equal(bent.astype(np.int64), exp)
 
 
 def _status(w):
