@@ -1137,8 +1137,12 @@ int xlds_grid(const BlobHeader& h) {
   return g > need ? g : need;
 }
 
-// The x-resident kernel runs when x and the partials leave at least 1 KiB of LDS.
-bool xlds_fits(const BlobHeader& h, int nb) { return xlds_fixed(h, xlds_grid(h), nb) + 1024 <= kLdsBytes; }
+// The x-resident kernel runs when workgroups get two or more tiles (x is
+// then reused across tiles; with one tile per workgroup loading x next to the
+// codes is faster) and x and the partials leave at least 1 KiB of LDS.
+bool xlds_fits(const BlobHeader& h, int nb) {
+  return h.tiles > xlds_grid(h) && xlds_fixed(h, xlds_grid(h), nb) + 1024 <= kLdsBytes;
+}
 
 template <int FMT, int BITS, int NB>
 hipError_t launch_xlds(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {

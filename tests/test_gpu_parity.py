@@ -275,6 +275,10 @@ def test_batched_edge_cases(torch, fmt, bits, B):
         "k32": _custom(fmt, bits, 300, 32, [1] * 300, seed=3),
         "dense_csr_rows": _custom(fmt, bits, 9, 4096, [0, 700, 64, 65, 128, 320, 321, 1, 4096], seed=4),
         "max_k": _custom(fmt, bits, 5, 16384, [3, 0, 500, 7, 16384], seed=5),
+        # over 256 tiles, so workgroups own two or three tiles (x resident in LDS)
+        "multi_tile": _custom(fmt, bits, 8208, 384, [i % 6 for i in range(8208)], seed=6),
+        # the first workgroup's outliers exceed what its LDS holds
+        "csr_past_lds": _custom(fmt, bits, 4112, 1024, [1024] * 40 + [i % 4 for i in range(4072)], seed=7),
     }
     for label, f in cases.items():
         _say(f"[gpu] batched edge {fmt}{bits} B={B} {label} M={f['M']} K={f['K']} nnz={f['row_ptr'][-1]}")
