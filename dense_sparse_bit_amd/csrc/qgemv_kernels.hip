@@ -972,6 +972,228 @@ k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batch 1, 4-bit LUT codes: pair tables in LDS.
+//
+// A byte of an L4 chunk holds two codes, A (chunk column k) and B (column
+// 4 + k).  For each row the workgroup builds a 256-entry table that maps a
+// byte value to the FP16 pair (LUT[A], LUT[B]), so one 4-byte LDS read
+// decodes two codes.  The four K-groups of the MFMA A operand carry four
+// different tiles: lane l holds row l % 16 of tile 4g + l / 16 of the
+// workgroup (g = table region, at most two), so each lane reads its own
+// row's table.  The table of lane l sits at byte 4l of every 256-byte line
+// and line b holds byte value b, so the 64 lanes of a read always fall in 64
+// different banks, and one v_perm forms the address (4l, code byte, region)
+// straight from the code dword.  Column t of the B operand carries x only in
+// K-group t and zeros elsewhere, so MFMA column t sums the rows of tile t.
+//
+// x sits in LDS with each group of 8 columns in pair order (0,4,1,5,2,6,3,7),
+// the order in which the pair reads fill an A operand.  The work is cut into
+// units of one 256-byte quarter of a (tile, K-block) piece for each of the 4
+// tiles of a region; the units, region-major, are cut into 16 contiguous
+// runs, one per wave, and wave v writes its sums for region g to partial slot
+// v + g (distinct, because the runs are ordered).  Every output adds the slots
+// of the waves covering its region in wave order, then its outliers, so the
+// result does not depend on timing.
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ void __launch_bounds__(64 * kWaves)
+k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
+       const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
+       int Kp, int nkb, int tiles, uint32_t meta_bytes, int nnz, int ent_cap) {
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T0 = (int)((int64_t)blockIdx.x * tiles / gridDim.x);
+  const int T1 = (int)((int64_t)(blockIdx.x + 1) * tiles / gridDim.x);
+  const int TW = T1 - T0;  // at most 8
+  const int G = (TW + 3) >> 2;  // table regions
+  const int nrows = min(TW * 16, M - T0 * 16);
+  const int P = 4 * nkb;  // units per region
+  const int U = G * P;
+  const int u0 = w * U / kWaves, u1 = (w + 1) * U / kWaves;  // this wave's run
+
+  // LDS: tables [G][256 byte values][64 lanes] | xs [Kp] FP16, pair order | slots [16 + G][4 tiles][16 rows]
+  //      | csr [TW*16] | row_ptr [TW*16+1, padded] | group counter (padded) | CSR entries [ent_cap]
+  uint16_t* xs = (uint16_t*)(lds + G * 16384);
+  float* slots = (float*)(lds + G * 16384 + Kp / 2);
+  float* csr = slots + (kWaves + G) * 64;
+  int* rp_lds = (int*)(csr + TW * 16);
+  int* group_ctr = rp_lds + ((TW * 16 + 4) & ~3);
+  uint32_t* ent_lds = (uint32_t*)(group_ctr + 4);  // 16-byte aligned
+
+  // Prologue: every load is issued, then waited for once.
+  const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
+  const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                               rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
+                                         : 0;
+  const int ev = lane < 2 ? __builtin_amdgcn_raw_buffer_load_b32(rr, (T0 * 16 + (lane ? nrows : 0)) * 4, 0, 0) : 0;
+  // Table entries of byte values 16w .. 16w+15 for lane column `lane` of each
+  // region: A runs over LUT entries 8*bit2(w) .. +7 (one 16-byte piece), B
+  // over the two entries of LUT dword (w & 3) | 4*bit3(w).
+  const rsrc_t rl = make_rsrc(meta, meta_bytes);
+  u32x4_t la[2];
+  uint32_t lb[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int tile = T0 + 4 * g + (lane >> 4);
+    const bool has = g < G && tile < T1;
+    const uint32_t rowb = (uint32_t)(tile * 16 + (lane & 15)) * 32u;
+    la[g] = __builtin_amdgcn_raw_buffer_load_b128(rl, (int)(has ? rowb + 16u * ((w >> 2) & 1) : kOutOfRange), 0,
+                                                  kNonTemporal);
+    lb[g] = __builtin_amdgcn_raw_buffer_load_b32(
+        rl, (int)(has ? rowb + 4u * (uint32_t)((w & 3) | 4 * ((w >> 3) & 1)) : kOutOfRange), 0, kNonTemporal);
+  }
+  // x straight into LDS (columns past K read as 0); each thread reorders its own pieces below.
+  const rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
+  const int xpieces = Kp / 8;  // a multiple of 16
+  for (int i = w; 64 * i < xpieces; i += kWaves) {
+    const int piece = 64 * i + lane;
+    if (piece < xpieces)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xs + 512 * i), 16,
+                                               8 * piece < K ? piece * 16 : (int)kOutOfRange, 0, 0, 0);
+  }
+  const int E0 = __builtin_amdgcn_readlane(ev, 0), E1 = __builtin_amdgcn_readlane(ev, 1);
+  const int A0 = E0 & ~3;  // entries [A0, Acap) of the workgroup's run are copied into LDS
+  const int Acap = min(E1, A0 + ent_cap);
+  {
+    const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
+    const int pieces = (Acap - A0 + 3) >> 2;
+    for (int i = w; 64 * i < pieces; i += kWaves) {
+      const int piece = 64 * i + lane;
+      if (piece < pieces)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(ent_lds + 256 * i), 16,
+                                                 (A0 + 4 * piece) * 4, 0, 0, kNonTemporal);
+    }
+  }
+  // The code ring.  Lanes of tiles past T1 fall outside the resource and read 0.
+  const rsrc_t rc = make_rsrc(codes, (uint32_t)T1 * (uint32_t)nkb * 1024u);
+  const uint32_t lb0 = (uint32_t)((T0 + (lane >> 4)) * nkb) * 1024u + (uint32_t)(lane & 15) * 16u;
+  auto uoff = [&](int v) -> uint32_t {  // unit v: region v / P, quarter-block v % P
+    if (v >= u1) return kOutOfRange;
+    const int g = v >= P ? 1 : 0;
+    return lb0 + (uint32_t)(g * P) * 1024u + (uint32_t)(v - g * P) * 256u;
+  };
+  u32x4_t ring[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) ring[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)uoff(u0 + s), 0, kNonTemporal);
+
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  for (int i = w; 64 * i < xpieces; i += kWaves) {
+    const int piece = 64 * i + lane;
+    if (piece < xpieces) {
+      u32x4_t* q = (u32x4_t*)xs + piece;
+      const u32x4_t v = *q;
+      const u32x4_t o = {perm(v[2], v[0], 0x05040100u), perm(v[2], v[0], 0x07060302u), perm(v[3], v[1], 0x05040100u),
+                         perm(v[3], v[1], 0x07060302u)};
+      *q = o;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (g < G) {
+      uint32_t* tg = lds + g * 16384 + 16 * w * 64 + lane;
+      const uint32_t a[4] = {la[g][0], la[g][1], la[g][2], la[g][3]};
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        tg[64 * i] = perm(lb[g], a[(i & 7) >> 1], ((i & 1) ? 0x0302u : 0x0100u) | ((i & 8) ? 0x07060000u : 0x05040000u));
+    }
+  }
+  if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
+  if (threadIdx.x == 0) *group_ctr = 0;
+  __syncthreads();
+
+  // The stream.
+  const int tq = lane >> 4, mq = lane & 15;
+  const bool on = mq == tq;  // B-operand lanes that carry x
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  half8_t bx = {0, 0, 0, 0, 0, 0, 0, 0};
+  int gc = u0 >= P ? 1 : 0;
+  auto flush = [&]() {  // acc[i]: row 4*(lane/16) + i of tile lane % 16 of region gc
+    float* d = slots + (w + gc) * 64;
+    if (mq < 4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[mq * 16 + 4 * tq + i] = acc[i];
+  };
+  for (int uu = u0; uu < u1; uu += R) {
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const int v = uu + s;
+      if (v < u1) {
+        const int g = v >= P ? 1 : 0;
+        if (g != gc) {
+          flush();
+          acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+          gc = g;
+        }
+        const uint32_t base = ((uint32_t)g << 16) | ((uint32_t)lane << 2);
+        const half8_t* xp = (const half8_t*)(xs + 32 * (v - g * P));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t a[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            a[k] = *(const uint32_t*)((const uint8_t*)lds + perm(ring[s][i], base, 0x0C020400u + ((uint32_t)k << 8)));
+          if (on) bx = xp[i];
+          acc = mfma(h8(a[0], a[1], a[2], a[3]), bx, acc);
+        }
+      }
+      // Unconditional, so that every slot has the same loads behind it (a
+      // load past the run is out of range).
+      ring[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)uoff(v + R), 0, kNonTemporal);
+    }
+  }
+  if (u0 < u1) flush();
+
+  // Outliers, before the barrier, by the waves that finish first: groups of
+  // four CSR rows from an LDS counter, one DPP row of 16 lanes per CSR row,
+  // a lane taking every 16th outlier of its row.
+  {
+    const int sl = lane & 15, rq = lane >> 4;
+    for (;;) {
+      int gi = 0;
+      if (lane == 0) gi = lds_fetch_add(group_ctr, 1);
+      gi = __builtin_amdgcn_readfirstlane(gi);
+      if (4 * gi >= nrows) break;
+      const int r = 4 * gi + rq;
+      const bool real = r < nrows;
+      const int p0 = real ? rp_lds[r] : 0, p1 = real ? rp_lds[r + 1] : 0;
+      const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
+      float v = 0.f;
+      auto term = [&](uint32_t e) {
+        const uint32_t c = e & 0xFFFFu;
+        const uint32_t pc = (c & ~7u) | ((c & 3u) << 1) | ((c >> 2) & 1u);  // pair-order position
+        v = dot2(e >> 16, (uint32_t)xs[pc], v);
+      };
+      for (int p = p0 + sl; p < pm; p += 16) term(ent_lds[p - A0]);
+      int p = max(p0, Acap) + sl;
+      for (; p + 48 < p1; p += 64) {  // four outliers from HBM in flight
+        uint32_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = entries[p + 16 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) term(e[u]);
+      }
+      for (; p < p1; p += 16) term(entries[p]);
+      v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+      v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+      v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror
+      v += dpp_mov<0x140, 0xF>(v);  // row_mirror: every lane of the row holds the sum
+      if (real && sl == 0) csr[r] = v;
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < nrows; r += 64 * kWaves) {
+    const int g = r >> 6;  // local row r = 64 g + 16 t + m
+    float v = 0.f;
+    for (int u = 0; u < kWaves; ++u) {
+      const int c0 = u * U / kWaves, c1 = (u + 1) * U / kWaves;
+      if (c0 < c1 && c0 < (g + 1) * P && c1 > g * P) v += slots[(u + g) * 64 + (r & 63)];
+    }
+    y[T0 * 16 + r] = v + csr[r];
+  }
+}
+
 // Debug: decode the blob's codes back to canonical order, one thread per 32-code chunk.
 template <int FMT, int BITS>
 __global__ void __launch_bounds__(256)
@@ -1167,9 +1389,54 @@ hipError_t launch_xlds(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   return hipGetLastError();
 }
 
+// Pair-table kernel (4-bit LUT codes, batch 1): at most 8 tiles per
+// workgroup, so that the tables fit in two 64 KiB regions.
+int pair_grid(const BlobHeader& h) {
+  const int g = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
+  const int need = (h.tiles + 7) / 8;
+  return g > need ? g : need;
+}
+
+// LDS of the pair-table kernel apart from the CSR entries: tables, x, partial
+// slots, CSR sums, row_ptr slice and the CSR group counter.
+size_t pair_fixed(const BlobHeader& h, int grid) {
+  const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
+  const size_t regions = (tw + 3) / 4;
+  return regions * 65536 + (size_t)h.Kp * 2 + (kWaves + regions) * 64 * 4 + tw * 16 * 4 +
+         ((tw * 16 + 4) & ~(size_t)3) * 4 + 16;
+}
+
+bool pair_fits(const BlobHeader& h) {
+  return h.format == QGEMV_FMT_LUT && h.bits == 4 && pair_fixed(h, pair_grid(h)) + 1024 <= kLdsBytes;
+}
+
+hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+  constexpr int R = 4;  // code ring slots per wave
+  const BlobHeader& h = p->h;
+  const int grid = pair_grid(h);
+  const size_t fixed = pair_fixed(h, grid);
+  size_t cap = kLdsBytes - fixed;  // CSR entries staged in LDS
+  if (cap > kEntCapBytes) cap = kEntCapBytes;
+  cap &= ~(size_t)1023;  // whole 1 KiB wave copies
+  size_t lds = fixed + cap;
+  if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_pair<R>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
+  hipLaunchKernelGGL((k_pair<R>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
+                     (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
+                     (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, meta_bytes,
+                     (int)h.nnz, (int)(cap / 4));
+  return hipGetLastError();
+}
+
 template <int FMT, int BITS>
 hipError_t launch_run(const qgemv_plan* p, const uint16_t* x, float* y, int batch, hipStream_t st) {
-  if (batch == 1) return launch_stream<FMT, BITS, 1>(p, x, y, st);
+  if (batch == 1) {
+    if (FMT == QGEMV_FMT_LUT && BITS == 4 && pair_fits(p->h)) return launch_pair(p, x, y, st);
+    return launch_stream<FMT, BITS, 1>(p, x, y, st);
+  }
   if (batch == 8)
     return xlds_fits(p->h, 8) ? launch_xlds<FMT, BITS, 8>(p, x, y, st) : launch_stream<FMT, BITS, 8>(p, x, y, st);
   return xlds_fits(p->h, 16) ? launch_xlds<FMT, BITS, 16>(p, x, y, st) : launch_stream<FMT, BITS, 16>(p, x, y, st);
