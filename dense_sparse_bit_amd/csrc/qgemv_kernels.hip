@@ -1000,7 +1000,7 @@ template <int R>
 __global__ void __launch_bounds__(64 * kWaves)
 k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
        const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
-       int Kp, int nkb, int tiles, uint32_t meta_bytes, int nnz, int ent_cap) {
+       int Kp, int nkb, int tiles, uint32_t meta_bytes) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1011,23 +1011,24 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   const int nrows = min(TW * 16, M - T0 * 16);
   const int P = 4 * nkb;  // units per region
   const int U = G * P;
-  const int u0 = w * U / kWaves, u1 = (w + 1) * U / kWaves;  // this wave's run
+  auto run_bound = [&](int v) { return v * U / kWaves; };
+  const int u0 = run_bound(w), u1 = run_bound(w + 1);  // this wave's run
 
   // LDS: tables [G][256 byte values][64 lanes] | xs [Kp] FP16, pair order | slots [16 + G][4 tiles][16 rows]
-  //      | csr [TW*16] | row_ptr [TW*16+1, padded] | group counter (padded) | CSR entries [ent_cap]
+  //      | csr [TW*16] | row_ptr [TW*16+1, padded] | group counter
   uint16_t* xs = (uint16_t*)(lds + G * 16384);
   float* slots = (float*)(lds + G * 16384 + Kp / 2);
   float* csr = slots + (kWaves + G) * 64;
   int* rp_lds = (int*)(csr + TW * 16);
   int* group_ctr = rp_lds + ((TW * 16 + 4) & ~3);
-  uint32_t* ent_lds = (uint32_t*)(group_ctr + 4);  // 16-byte aligned
 
-  // Prologue: every load is issued, then waited for once.
+  // Prologue.  What goes to LDS is loaded first, then the code ring; storing
+  // the staged pieces waits for them alone, and the barrier (LDS only) lets
+  // the ring loads run on into the stream.
   const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
   const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
                                                rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
                                          : 0;
-  const int ev = lane < 2 ? __builtin_amdgcn_raw_buffer_load_b32(rr, (T0 * 16 + (lane ? nrows : 0)) * 4, 0, 0) : 0;
   // Table entries of byte values 16w .. 16w+15 for lane column `lane` of each
   // region: A runs over LUT entries 8*bit2(w) .. +7 (one 16-byte piece), B
   // over the two entries of LUT dword (w & 3) | 4*bit3(w).
@@ -1044,32 +1045,21 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
     lb[g] = __builtin_amdgcn_raw_buffer_load_b32(
         rl, (int)(has ? rowb + 4u * (uint32_t)((w & 3) | 4 * ((w >> 3) & 1)) : kOutOfRange), 0, kNonTemporal);
   }
-  // x straight into LDS (columns past K read as 0); each thread reorders its own pieces below.
+  // x: 8-column pieces tid and tid + 1024 (Kp <= 16384); columns past K read as 0.
   const rsrc_t rx = make_rsrc(x, (uint32_t)K * 2u);
-  const int xpieces = Kp / 8;  // a multiple of 16
-  for (int i = w; 64 * i < xpieces; i += kWaves) {
-    const int piece = 64 * i + lane;
-    if (piece < xpieces)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xs + 512 * i), 16,
-                                               8 * piece < K ? piece * 16 : (int)kOutOfRange, 0, 0, 0);
+  const int xpieces = Kp / 8;
+  u32x4_t xv[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int piece = (int)threadIdx.x + 1024 * k;
+    xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, piece < xpieces ? piece * 16 : (int)kOutOfRange, 0, 0);
   }
-  const int E0 = __builtin_amdgcn_readlane(ev, 0), E1 = __builtin_amdgcn_readlane(ev, 1);
-  const int A0 = E0 & ~3;  // entries [A0, Acap) of the workgroup's run are copied into LDS
-  const int Acap = min(E1, A0 + ent_cap);
-  {
-    const rsrc_t re = make_rsrc(entries, (uint32_t)nnz * 4);
-    const int pieces = (Acap - A0 + 3) >> 2;
-    for (int i = w; 64 * i < pieces; i += kWaves) {
-      const int piece = 64 * i + lane;
-      if (piece < pieces)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(ent_lds + 256 * i), 16,
-                                                 (A0 + 4 * piece) * 4, 0, 0, kNonTemporal);
-    }
-  }
-  // The code ring.  Lanes of tiles past T1 fall outside the resource and read 0.
+  __builtin_amdgcn_sched_barrier(0);  // keep the ring loads behind the staged ones
+  // The code ring.  Unit v: region g = v / P, quarter-block v % P; lanes of
+  // tiles past T1 fall outside the resource and read 0.
   const rsrc_t rc = make_rsrc(codes, (uint32_t)T1 * (uint32_t)nkb * 1024u);
   const uint32_t lb0 = (uint32_t)((T0 + (lane >> 4)) * nkb) * 1024u + (uint32_t)(lane & 15) * 16u;
-  auto uoff = [&](int v) -> uint32_t {  // unit v: region v / P, quarter-block v % P
+  auto uoff = [&](int v) -> uint32_t {
     if (v >= u1) return kOutOfRange;
     const int g = v >= P ? 1 : 0;
     return lb0 + (uint32_t)(g * P) * 1024u + (uint32_t)(v - g * P) * 256u;
@@ -1077,17 +1067,20 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   u32x4_t ring[R];
 #pragma unroll
   for (int s = 0; s < R; ++s) ring[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)uoff(u0 + s), 0, kNonTemporal);
+  // The table loads are used only for regions that exist; this use keeps
+  // them ahead of the ring (the wait it implies is the one below).
+  asm volatile("" ::"v"(la[0]), "v"(lb[0]), "v"(la[1]), "v"(lb[1]));
 
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  for (int i = w; 64 * i < xpieces; i += kWaves) {
-    const int piece = 64 * i + lane;
-    if (piece < xpieces) {
-      u32x4_t* q = (u32x4_t*)xs + piece;
-      const u32x4_t v = *q;
-      const u32x4_t o = {perm(v[2], v[0], 0x05040100u), perm(v[2], v[0], 0x07060302u), perm(v[3], v[1], 0x05040100u),
-                         perm(v[3], v[1], 0x07060302u)};
-      *q = o;
-    }
+  // x in pair order: (0,4,1,5,2,6,3,7) in each 8-column group.  A piece past
+  // x goes to the first 16 bytes after it (partial slot 0, which is written
+  // before it is read); unconditional stores keep the x loads ahead of the ring.
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int piece = (int)threadIdx.x + 1024 * k;
+    const u32x4_t v = xv[k];
+    const u32x4_t o = {perm(v[2], v[0], 0x05040100u), perm(v[2], v[0], 0x07060302u), perm(v[3], v[1], 0x05040100u),
+                       perm(v[3], v[1], 0x07060302u)};
+    ((u32x4_t*)xs)[min(piece, xpieces)] = o;
   }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -1101,7 +1094,7 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   }
   if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
   if (threadIdx.x == 0) *group_ctr = 0;
-  __syncthreads();
+  lds_barrier();
 
   // The stream.
   const int tq = lane >> 4, mq = lane & 15;
@@ -1147,7 +1140,9 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
 
   // Outliers, before the barrier, by the waves that finish first: groups of
   // four CSR rows from an LDS counter, one DPP row of 16 lanes per CSR row,
-  // a lane taking every 16th outlier of its row.
+  // a lane taking every 16th outlier of its row from HBM, four at a time;
+  // four DPP steps add the 16 lanes.  A row's sum is the same whichever wave
+  // takes it.
   {
     const int sl = lane & 15, rq = lane >> 4;
     for (;;) {
@@ -1158,16 +1153,14 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
       const int r = 4 * gi + rq;
       const bool real = r < nrows;
       const int p0 = real ? rp_lds[r] : 0, p1 = real ? rp_lds[r + 1] : 0;
-      const int pm = min(p1, Acap);  // [p0, pm) is in LDS, [max(p0, Acap), p1) only in HBM
       float v = 0.f;
       auto term = [&](uint32_t e) {
         const uint32_t c = e & 0xFFFFu;
         const uint32_t pc = (c & ~7u) | ((c & 3u) << 1) | ((c >> 2) & 1u);  // pair-order position
         v = dot2(e >> 16, (uint32_t)xs[pc], v);
       };
-      for (int p = p0 + sl; p < pm; p += 16) term(ent_lds[p - A0]);
-      int p = max(p0, Acap) + sl;
-      for (; p + 48 < p1; p += 64) {  // four outliers from HBM in flight
+      int p = p0 + sl;
+      for (; p + 48 < p1; p += 64) {  // four outliers in flight
         uint32_t e[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) e[u] = entries[p + 16 * u];
@@ -1187,7 +1180,7 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
     const int g = r >> 6;  // local row r = 64 g + 16 t + m
     float v = 0.f;
     for (int u = 0; u < kWaves; ++u) {
-      const int c0 = u * U / kWaves, c1 = (u + 1) * U / kWaves;
+      const int c0 = run_bound(u), c1 = run_bound(u + 1);
       if (c0 < c1 && c0 < (g + 1) * P && c1 > g * P) v += slots[(u + g) * 64 + (r & 63)];
     }
     y[T0 * 16 + r] = v + csr[r];
@@ -1397,9 +1390,9 @@ int pair_grid(const BlobHeader& h) {
   return g > need ? g : need;
 }
 
-// LDS of the pair-table kernel apart from the CSR entries: tables, x, partial
-// slots, CSR sums, row_ptr slice and the CSR group counter.
-size_t pair_fixed(const BlobHeader& h, int grid) {
+// LDS of the pair-table kernel: tables, x, partial slots, CSR sums, row_ptr
+// slice and the CSR group counter.
+size_t pair_lds(const BlobHeader& h, int grid) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
   const size_t regions = (tw + 3) / 4;
   return regions * 65536 + (size_t)h.Kp * 2 + (kWaves + regions) * 64 * 4 + tw * 16 * 4 +
@@ -1407,18 +1400,14 @@ size_t pair_fixed(const BlobHeader& h, int grid) {
 }
 
 bool pair_fits(const BlobHeader& h) {
-  return h.format == QGEMV_FMT_LUT && h.bits == 4 && pair_fixed(h, pair_grid(h)) + 1024 <= kLdsBytes;
+  return h.format == QGEMV_FMT_LUT && h.bits == 4 && h.Kp <= 16384 && pair_lds(h, pair_grid(h)) <= kLdsBytes;
 }
 
 hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
   constexpr int R = 4;  // code ring slots per wave
   const BlobHeader& h = p->h;
   const int grid = pair_grid(h);
-  const size_t fixed = pair_fixed(h, grid);
-  size_t cap = kLdsBytes - fixed;  // CSR entries staged in LDS
-  if (cap > kEntCapBytes) cap = kEntCapBytes;
-  cap &= ~(size_t)1023;  // whole 1 KiB wave copies
-  size_t lds = fixed + cap;
+  size_t lds = pair_lds(h, grid);
   if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)k_pair<R>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
@@ -1426,8 +1415,7 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
   hipLaunchKernelGGL((k_pair<R>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
-                     (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, meta_bytes,
-                     (int)h.nnz, (int)(cap / 4));
+                     (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, meta_bytes);
   return hipGetLastError();
 }
 
