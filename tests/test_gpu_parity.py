@@ -191,21 +191,23 @@ def _rows_of(f, rng, extra=()):
     return np.unique(np.concatenate([[0, 1, M - 2, M - 1], heavy, pick, np.asarray(extra, np.int64)]))
 
 
+@pytest.mark.parametrize("fmt,bits", [("lut", 4), ("lut", 3), ("uniform", 3), ("uniform", 4)])
 @pytest.mark.parametrize("label,M,K,heavy", [
-    ("tw8_ragged", 32768 - 5, 256, 0),      # 8 tiles per workgroup, two table regions, short last tile
-    ("tw5", 16 * 256 * 5 - 3, 384, 0),      # second region holds one tile
-    ("tw3_tw4", 16 * (256 * 3 + 100), 512, 0),  # 3 or 4 tiles per workgroup, one region
-    ("csr_past_lds", 16 * 256 * 5, 4096, 1000),  # CSR of workgroup 0 larger than its LDS copy
+    ("tw8_ragged", 32768 - 5, 256, 0),      # 8 tiles per workgroup (two LUT-4 table regions), short last tile
+    ("tw5", 16 * 256 * 5 - 3, 384, 0),      # 5 tiles: the second LUT-4 region holds one tile
+    ("tw3_tw4", 16 * (256 * 3 + 100), 512, 0),  # 3 or 4 tiles per workgroup
+    ("csr_heavy", 16 * 256 * 5, 4096, 1000),  # 40 rows of 1000 outliers in workgroup 0 (past any LDS copy)
 ])
-def test_lut4_multi_tile_workgroups(torch, label, M, K, heavy):
-    """Batch-1 LUT-4 shapes whose workgroups hold several tiles (pair-table kernel)."""
+def test_b1_multi_tile_workgroups(torch, fmt, bits, label, M, K, heavy):
+    """Batch-1 shapes whose workgroups hold several tiles (the pair-table kernel
+    for LUT-4 codes, the streaming kernel for the others)."""
     rng = np.random.default_rng(21)
     row_nnz = [int(v) for v in rng.integers(0, 4, size=M)]
     row_nnz[7] = K  # a full row
     for r in range(40):
         row_nnz[16 + r] = heavy if heavy else row_nnz[16 + r]
-    f = _custom("lut", 4, M, K, row_nnz, seed=11)
-    _say(f"[gpu] lut4 multi-tile {label} M={M} K={K} nnz={f['row_ptr'][-1]}")
+    f = _custom(fmt, bits, M, K, row_nnz, seed=11)
+    _say(f"[gpu] b1 multi-tile {fmt}{bits} {label} M={M} K={K} nnz={f['row_ptr'][-1]}")
     x16 = np.random.default_rng(12).standard_normal((1, K)).astype(np.float16)
     plan = qgemv.QGemv(f)
     y1 = run_b1(torch, plan, x16)
