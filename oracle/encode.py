@@ -3,7 +3,9 @@
 Test infrastructure only (see the package docstring).
 
 Step order follows the pages:
-  1. outlier pick                      [SpQR] "Qu'est-ce qu'un poids outlier ?"
+  1. outlier pick                      [SpQR] "Qu'est-ce qu'un poids outlier ?" (magnitude)
+                                       [SqLLM] "Sélection des outliers" (sensitivity-weighted error)
+                                       [Babai/GPTQ] SSQR (overflows of shrunk uniform grids)
   2. dense part with holes, quantized  [SpQR] "La solution SpQR : décomposition sparse + dense",
                                               "Quantification d'un modèle" (wbits, groupsize 16)
                                        [SqLLM] "Non-uniform quantization via Lloyd-Max optimisé"
@@ -42,6 +44,44 @@ def pick_outliers(W16: np.ndarray, n: int) -> np.ndarray:
     mask = np.zeros(a.size, dtype=bool)
     if n > 0:
         order = np.argsort(-a, kind="stable")[:n]
+        mask[order] = True
+    return mask.reshape(W16.shape)
+
+
+def first_pass_error(W16: np.ndarray, sens: np.ndarray, bits: int) -> np.ndarray:
+    """Per-weight sensitivity-weighted error s_j (w_ij - q(w_ij))^2 of a first-pass LUT.
+
+    [SqLLM] "Sélection des outliers": the criterion is the quantization error
+    weighted by the weight's sensitivity.  Reading: q is the row's LUT fitted
+    by lloyd_row over all of the row's weights (no holes yet), rounded to FP16,
+    each weight taking its nearest entry (ties: lower entry).
+    """
+    M, K = W16.shape
+    W = W16.astype(np.float64)
+    s = np.asarray(sens, dtype=np.float64)
+    err = np.zeros((M, K))
+    for i in range(M):
+        cent, _ = lloyd_row(W[i], s, 1 << bits)
+        tab = np.sort(cent.astype(np.float16), kind="stable").astype(np.float64)
+        err[i] = s * (W[i] - tab[nearest(W[i], tab)]) ** 2
+    return err
+
+
+def pick_outliers_sensitivity(W16: np.ndarray, sens: np.ndarray, bits: int, n: int) -> np.ndarray:
+    """Boolean mask of the n weights of largest sensitivity-weighted first-pass error.
+
+    [SqLLM] "Sélection des outliers": a weight goes to the sparse part when
+    s_i (w_i - q(w_i))^2 exceeds a threshold, so a moderate weight of very
+    high sensitivity can be extracted too, not only large ones.  Reading: the
+    threshold is the one that extracts exactly n weights (the workload's
+    density), i.e. the n largest errors, ties to the lower row-major index.
+    The LUT is then fitted again without these weights (quant_lut with them
+    as holes), as the dense part is quantized after the decomposition.
+    """
+    e = first_pass_error(W16, sens, bits).ravel()
+    mask = np.zeros(e.size, dtype=bool)
+    if n > 0:
+        order = np.argsort(-e, kind="stable")[:n]
         mask[order] = True
     return mask.reshape(W16.shape)
 
@@ -91,6 +131,72 @@ def quant_uniform(W16: np.ndarray, hole: np.ndarray, bits: int, group: int):
     return (q.reshape(M, K).astype(np.uint8),
             scale.astype(np.float16),
             z.astype(np.float16))
+
+
+# --------------------------------------------------------------------------
+# 2a'. SSQR: shrunk uniform grids, overflowing weights to the sparse part
+# --------------------------------------------------------------------------
+def quant_uniform_scaled(W16: np.ndarray, bits: int, group: int, alpha: float):
+    """Uniform group quantization on a grid shrunk by alpha; overflows become outliers.
+
+    [Babai/GPTQ] "3. Applications Pratiques et Algorithmes", SSQR: a scheme
+    that tolerates overflow -- weights that do not fit the integer grid are
+    kept in full precision in the sparse part instead of being clipped.
+
+    Per group, with L = 2^bits - 1, over all of the group's values (0 included):
+      lo = min(0, min w), hi = max(0, max w)
+      if hi == lo: scale = 1, z = 0 (nothing overflows)
+      else: scale = fp16(alpha * (hi - lo) / L)  (2^-24 if that rounds to 0)
+            z = clamp(rint(-alpha * lo / scale), 0, L)
+      t = rint(w / scale) + z; a weight overflows when t < 0 or t > L.
+      q = t for the others; q = z at overflows (holes, decoding to exactly 0).
+    Readings: one factor alpha for the whole matrix scales every group's
+    min-max grid about zero; the zero point is the integer nearest to the
+    shrunk lower end.
+
+    Returns (codes uint8 [M, K], scales fp16 [M, K/group], zeros fp16 [M, K/group],
+    overflow mask bool [M, K]).
+    """
+    M, K = W16.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    L = (1 << bits) - 1
+    w = W16.astype(np.float64).reshape(M, G, group)
+    lo = np.minimum(0.0, w.min(axis=2))
+    hi = np.maximum(0.0, w.max(axis=2))
+    flat = hi == lo
+    scale = f16(np.where(flat, 1.0, alpha * (hi - lo) / L))
+    scale = np.where(scale == 0.0, FP16_MIN_SUBNORMAL, scale)
+    z = np.where(flat, 0.0, np.clip(np.rint(-alpha * lo / scale), 0, L))
+    t = np.rint(w / scale[:, :, None]) + z[:, :, None]
+    over = (t < 0) | (t > L)
+    q = np.where(over, z[:, :, None], t)
+    return (q.reshape(M, K).astype(np.uint8), scale.astype(np.float16), z.astype(np.float16),
+            over.reshape(M, K))
+
+
+def ssqr_alpha(W16: np.ndarray, bits: int, group: int, n: int, iters: int = 40) -> float:
+    """Binary search for the grid factor that meets the outlier budget.
+
+    [Babai/GPTQ] "3. Applications Pratiques et Algorithmes", SSQR: a binary
+    search adjusts the scales to reach a target outlier density.  Reading:
+    the result is the smallest alpha in (0, 1] (to `iters` halvings) whose
+    overflow count is at most n, i.e. the finest grids within the budget; the
+    count falls as alpha grows.  Returns 1.0 if even alpha = 1 overflows more
+    than n times.
+    """
+    count = lambda a: int(quant_uniform_scaled(W16, bits, group, a)[3].sum())
+    if count(1.0) > n:
+        return 1.0
+    lo_a, hi_a = 0.0, 1.0
+    for _ in range(iters):
+        mid = 0.5 * (lo_a + hi_a)
+        if count(mid) <= n:
+            hi_a = mid
+        else:
+            lo_a = mid
+    return hi_a
 
 
 # --------------------------------------------------------------------------
@@ -225,8 +331,13 @@ def build_csr(W16: np.ndarray, hole: np.ndarray, D: np.ndarray):
 # Whole encoder
 # --------------------------------------------------------------------------
 def encode(W16: np.ndarray, bits: int, fmt: str, n_outliers: int, group: int = 16,
-           sens: np.ndarray | None = None) -> dict:
+           sens: np.ndarray | None = None, pick: str = "magnitude") -> dict:
     """Encode an FP16 matrix into the canonical dense-and-sparse format.
+
+    pick: "magnitude" (pick_outliers), "sensitivity" (pick_outliers_sensitivity,
+    LUT format only: it needs the sensitivities and a first-pass LUT) or "ssqr"
+    (uniform format only: the overflows of the grids ssqr_alpha finds for a
+    budget of n_outliers, which are then the outliers and the grids the dense part).
 
     Returns a dict with the fields of the canonical format:
       M, K, bits, fmt, group, codes (uint8 [M,K], unpacked), codes_packed
@@ -235,11 +346,29 @@ def encode(W16: np.ndarray, bits: int, fmt: str, n_outliers: int, group: int = 1
     """
     from .gemv import decode
     M, K = W16.shape
-    hole = pick_outliers(W16, n_outliers)
+    ssqr = None
+    if pick == "magnitude":
+        hole = pick_outliers(W16, n_outliers)
+    elif pick == "ssqr":
+        if fmt != "uniform":
+            raise ValueError("the SSQR pick needs the uniform format")
+        alpha = ssqr_alpha(W16, bits, group, n_outliers)
+        ssqr = quant_uniform_scaled(W16, bits, group, alpha)
+        hole = ssqr[3]
+    elif pick == "sensitivity":
+        if fmt != "lut" or sens is None:
+            raise ValueError("the sensitivity pick needs the LUT format and a sensitivity vector")
+        hole = pick_outliers_sensitivity(W16, np.asarray(sens, dtype=np.float64), bits, n_outliers)
+    else:
+        raise ValueError(pick)
     out = {"M": M, "K": K, "bits": bits, "fmt": fmt, "group": group if fmt == "uniform" else 0,
            "mask": hole}
     if fmt == "uniform":
-        codes, scales, zeros = quant_uniform(W16, hole, bits, group)
+        if ssqr is not None:
+            codes, scales, zeros = ssqr[:3]
+            out["alpha"] = alpha
+        else:
+            codes, scales, zeros = quant_uniform(W16, hole, bits, group)
         out.update(scales=scales, zeros=zeros)
     elif fmt == "lut":
         if sens is None:

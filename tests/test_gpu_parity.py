@@ -114,6 +114,42 @@ def test_small_oracle_encoded(torch, name, M, K):
     plan.close()
 
 
+@pytest.mark.parametrize("name,M,K", [("mlp7b_lut3", 64, 4096), ("mlp70b_lut4", 40, 2080)])
+def test_small_sensitivity_pick(torch, name, M, K):
+    """Encodings whose outliers come from the sensitivity-weighted error pick."""
+    wl = WORKLOADS[name]
+    W, _ = make_weights(wl, 0, M, K)
+    M_, K_ = W.shape
+    x16 = make_x(wl, 1, K_, 0, M_)
+    enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M_, K_), 16,
+                        sens=x16[0].astype(np.float64) ** 2, pick="sensitivity")
+    _say(f"[gpu] sensitivity pick {name} M={M_} K={K_} nnz={enc['row_ptr'][-1]}")
+    plan = qgemv.QGemv(enc)
+    assert np.array_equal(plan.debug_unpack().cpu().numpy(), enc["codes"])
+    check_y(run_b1(torch, plan, x16), enc, x16)
+    plan.close()
+
+
+@pytest.mark.parametrize("name,M,K,budget", [("attn7b_u3", 64, 4096, None), ("tiny_u4", 48, 512, None),
+                                             ("tiny_u4", 40, 256, "all")])
+def test_small_ssqr(torch, name, M, K, budget):
+    """Encodings from the SSQR grid search (overflows of shrunk grids to the
+    sparse part); 'all' makes every nonzero weight an outlier."""
+    wl = WORKLOADS[name]
+    W, _ = make_weights(wl, 0, M, K)
+    M_, K_ = W.shape
+    n = M_ * K_ if budget == "all" else outlier_count(wl, M_, K_)
+    enc = encode.encode(W, wl.bits, "uniform", n, 16, pick="ssqr")
+    x16 = make_x(wl, 1, K_, 0, M_)
+    _say(f"[gpu] ssqr {name} M={M_} K={K_} alpha={enc['alpha']:.6f} nnz={enc['row_ptr'][-1]}")
+    plan = qgemv.QGemv(enc)
+    assert np.array_equal(plan.debug_unpack().cpu().numpy(), enc["codes"])
+    check_y(run_b1(torch, plan, x16), enc, x16)
+    xb = make_x(wl, 8, K_, 0, M_)
+    check_y(run_bn(torch, plan, xb), enc, xb)
+    plan.close()
+
+
 FULL_CASES = [
     ("tiny_u4", 0), ("attn7b_u3", 0), ("mlp7b_lut3", 0), ("mlp70b_lut4", 0),
     ("block7b_u3", 0), ("block7b_u3", 4), ("block7b_u3", 6),

@@ -460,3 +460,212 @@ def test_extra_bits_per_weight_squeezellm_order_of_magnitude():
         assert 0.05 < bpw < 0.5
     assert accounting.dense_bpw(3, "lut", 4096) == pytest.approx(3.03125)
     assert accounting.dense_bpw(3, "uniform", 4096, 16) == 5.0
+
+
+# ---------------------------------------------------------------------------
+# Sensitivity-based outlier pick ([SqLLM] "Sélection des outliers")
+# ---------------------------------------------------------------------------
+def _loop_first_pass_error(W16, sens, bits):
+    """s_j (w - q(w))^2 with q the nearest entry of the row's FP16 first-pass table, by plain loops."""
+    M, K = W16.shape
+    W = W16.astype(np.float64)
+    out = np.zeros((M, K))
+    for i in range(M):
+        cent, _ = encode.lloyd_row(W[i], np.asarray(sens, np.float64), 1 << bits)
+        tab = sorted(float(v) for v in cent.astype(np.float16))
+        for j in range(K):
+            best = min(tab, key=lambda c: abs(W[i, j] - c))
+            out[i, j] = sens[j] * (W[i, j] - best) ** 2
+    return out
+
+
+def check_pick_minimizes_remaining_error(W16, sens, bits, n):
+    """Extracting the picked weights leaves the least weighted first-pass error of
+    all n-subsets: the pages' picked weights carry most of the potential error."""
+    import itertools
+    e = _loop_first_pass_error(W16, sens, bits).ravel()
+    mask = encode.pick_outliers_sensitivity(W16, sens, bits, n).ravel()
+    assert mask.sum() == n
+    got = e[~mask].sum()
+    best = min(e.sum() - sum(e[list(c)]) for c in itertools.combinations(range(e.size), n))
+    assert got <= best + 1e-15 * max(1.0, abs(best)), (got, best)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_sensitivity_pick_minimizes_remaining_error(seed):
+    rng = np.random.default_rng(seed)
+    W16 = (rng.standard_normal((2, 8)) * 0.05).astype(np.float16)
+    sens = rng.uniform(0.0, 3.0, size=8)
+    check_pick_minimizes_remaining_error(W16, sens, 2, 3)
+
+
+def test_sensitivity_pick_catches_smallest_first(monkeypatch):
+    orig = encode.first_pass_error
+    monkeypatch.setattr(encode, "first_pass_error", lambda W, s, b: -orig(W, s, b))
+    rng = np.random.default_rng(0)
+    W16 = (rng.standard_normal((2, 8)) * 0.05).astype(np.float16)
+    with pytest.raises(AssertionError):
+        check_pick_minimizes_remaining_error(W16, rng.uniform(0.0, 3.0, size=8), 2, 3)
+
+
+def _moderate_vs_large_row():
+    """One row: a bulk of N(0, 0.02) weights of sensitivity 1, twelve large
+    weights (0.5 .. 2.5) in columns of sensitivity 1e-6, and ten moderate
+    weights (-0.1 .. 0.1) in columns of sensitivity 100.  Each group outnumbers
+    the seven free entries of a 3-bit table, so neither can be fitted exactly."""
+    rng = np.random.default_rng(5)
+    K = 128
+    w = rng.standard_normal(K) * 0.02
+    s = np.ones(K)
+    lo = np.arange(40, 52)
+    w[lo] = np.linspace(0.5, 2.5, lo.size)
+    s[lo] = 1e-6
+    hi = np.arange(20, 30)
+    w[hi] = np.linspace(-0.1, 0.1, hi.size)
+    s[hi] = 100.0
+    return w.astype(np.float16)[None, :], s, hi, lo
+
+
+def check_moderate_high_sensitivity_picked(pick):
+    W16, s, hi, lo = _moderate_vs_large_row()
+    m = pick(W16, s, 3, 2)[0]
+    assert not m[lo].any(), "a large weight of negligible sensitivity was taken"
+    assert set(np.flatnonzero(m)) <= set(hi), "a pick is not a moderate weight of high sensitivity"
+
+
+def test_sensitivity_pick_takes_moderate_weight_of_high_sensitivity():
+    check_moderate_high_sensitivity_picked(encode.pick_outliers_sensitivity)
+    # the magnitude pick takes large weights instead
+    W16, s, hi, lo = _moderate_vs_large_row()
+    assert set(np.flatnonzero(encode.pick_outliers(W16, 2)[0])) <= set(lo)
+
+
+def test_sensitivity_pick_catches_dropped_sensitivity(monkeypatch):
+    orig = encode.first_pass_error
+    monkeypatch.setattr(encode, "first_pass_error", lambda W, s, b: orig(W, np.ones_like(s), b))
+    with pytest.raises(AssertionError):
+        check_moderate_high_sensitivity_picked(encode.pick_outliers_sensitivity)
+
+
+def test_sensitivity_pick_equal_sensitivity_takes_planted():
+    """With equal sensitivities the criterion is the plain squared error: with
+    twenty planted weights in 0.5 .. 2.5 per row, more than a 3-bit table can
+    fit, the twelve picked per row are all planted ones."""
+    rng = np.random.default_rng(2)
+    M, K = 3, 512
+    W = rng.standard_normal((M, K)) * 0.02
+    planted = np.zeros((M, K), dtype=bool)
+    for i in range(M):
+        cols = rng.choice(K, size=20, replace=False)
+        W[i, cols] = rng.uniform(0.5, 2.5, size=20) * rng.choice([-1.0, 1.0], size=20)
+        planted[i, cols] = True
+    m = encode.pick_outliers_sensitivity(W.astype(np.float16), np.ones(K), 3, 12 * M)
+    assert m.sum() == 12 * M
+    assert not (m & ~planted).any()
+
+
+def test_sensitivity_pick_encoding_is_exact_at_outliers():
+    """The encoding built on the sensitivity pick keeps the pages' invariants:
+    holes decode to 0 and dense + sparse reproduces every outlier exactly."""
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, 24, 256)
+    x = make_x(wl, 1, 256, 0, 24)
+    n = 40
+    enc = encode.encode(W, 3, "lut", n, sens=x[0].astype(np.float64) ** 2, pick="sensitivity")
+    assert int(enc["row_ptr"][-1]) == n
+    check_exact_outliers(W, enc)
+
+
+# ---------------------------------------------------------------------------
+# SSQR: overflow-tolerant uniform grids ([Babai/GPTQ] "3. Applications
+# Pratiques et Algorithmes")
+# ---------------------------------------------------------------------------
+def _ssqr_matrix(seed=0, M=8, K=64):
+    wl = WORKLOADS["attn7b_u3"]
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((M, K)) * 0.02
+    idx = rng.choice(M * K, size=6, replace=False)
+    W.flat[idx] = rng.uniform(0.3, 1.5, size=6) * rng.choice([-1.0, 1.0], size=6)
+    return W.astype(np.float16)
+
+
+def check_ssqr_grid(W16, bits, alpha):
+    """Inliers sit on the nearest point of their group's grid; overflows are
+    exactly the weights whose nearest grid point lies outside [0, 2^b - 1]."""
+    codes, scales, zeros, over = encode.quant_uniform_scaled(W16, bits, 16, alpha)
+    L = (1 << bits) - 1
+    M, K = W16.shape
+    w = W16.astype(np.float64)
+    for i in range(M):
+        for j in range(K):
+            s = float(scales[i, j // 16]); z = float(zeros[i, j // 16])
+            u = w[i, j] / s + z  # position on the integer grid
+            if over[i, j]:
+                assert u < -0.5 or u > L + 0.5, (i, j, u)
+                assert codes[i, j] == z
+            else:
+                assert 0 <= codes[i, j] <= L
+                assert abs(w[i, j] - s * (codes[i, j] - z)) <= 0.5 * s + 1e-12 * abs(w[i, j]), (i, j)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("alpha", [1.0, 0.6, 0.25])
+def test_ssqr_inliers_on_grid_overflows_outside(bits, alpha):
+    check_ssqr_grid(_ssqr_matrix(bits), bits, alpha)
+
+
+def test_ssqr_grid_catches_floor(monkeypatch):
+    monkeypatch.setattr(encode.np, "rint", np.floor)
+    with pytest.raises(AssertionError):
+        check_ssqr_grid(_ssqr_matrix(1), 3, 0.6)
+
+
+def check_ssqr_budget(W16, bits, n):
+    """The search keeps the overflow count within the budget, with the finest
+    grids that do: one search step lower, the budget is exceeded."""
+    a = encode.ssqr_alpha(W16, bits, 16, n)
+    count = lambda t: int(encode.quant_uniform_scaled(W16, bits, 16, t)[3].sum())
+    assert count(a) <= n
+    assert count(a - 2.0 ** -38) > n
+
+
+@pytest.mark.parametrize("n", [0, 3, 6, 40])
+def test_ssqr_search_meets_budget(n):
+    check_ssqr_budget(_ssqr_matrix(2), 3, n)
+
+
+def test_ssqr_search_catches_flipped_direction(monkeypatch):
+    orig = encode.quant_uniform_scaled
+    # a search that keeps the coarsest grid: report every overflow count as within budget
+    monkeypatch.setattr(encode, "quant_uniform_scaled",
+                        lambda W, b, g, a: orig(W, b, g, a)[:3] + (np.zeros(W.shape, dtype=bool),))
+    W16 = _ssqr_matrix(2)
+    with pytest.raises(AssertionError):
+        a = encode.ssqr_alpha(W16, 3, 16, 3)
+        assert orig(W16, 3, 16, a)[3].sum() <= 3
+
+
+def test_ssqr_all_sparse_is_plain_product():
+    """A budget of every weight: the grids shrink until all nonzero weights
+    overflow, the dense part decodes to 0 and y is the plain FP16 product."""
+    W16 = _ssqr_matrix(3)
+    M, K = W16.shape
+    enc = encode.encode(W16, 3, "uniform", M * K, pick="ssqr")
+    assert np.all(gemv.decode(enc) == 0.0)
+    x = np.random.default_rng(4).standard_normal((1, K)).astype(np.float16)
+    y, _ = gemv.gemv_rows(enc, x)
+    assert np.allclose(y, W16.astype(np.float64) @ x[0].astype(np.float64), rtol=0, atol=1e-12)
+
+
+def test_ssqr_no_budget_all_inliers():
+    W16 = _ssqr_matrix(4)
+    enc = encode.encode(W16, 4, "uniform", 0, pick="ssqr")
+    assert int(enc["row_ptr"][-1]) == 0
+    check_ssqr_grid(W16, 4, enc["alpha"])
+
+
+def test_ssqr_encoding_is_exact_at_outliers():
+    W16 = _ssqr_matrix(5, M=16, K=128)
+    enc = encode.encode(W16, 3, "uniform", 10, pick="ssqr")
+    assert 0 < int(enc["row_ptr"][-1]) <= 10
+    check_exact_outliers(W16, enc)
