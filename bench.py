@@ -48,6 +48,8 @@ WORKLOAD_NOTES = {
     "tiny_u4": "512x512, 4-bit codes + FP16 scale/zero per 16, 1% FP16 CSR outliers",
     "block7b_u3": "7B decoder block q,k,v,o 4096x4096, gate,up 11008x4096, down 4096x11008; 3-bit codes + "
                   "FP16 scale/zero per 16, 1% FP16 CSR outliers",
+    "mlp7b_bpdq3": "MLP up-proj 11008x4096, 3-bit BPDQ codes + 4 FP16 bit-plane coefficients per row and group of "
+                   "64, 0.45% FP16 CSR outliers",
 }
 DEFAULT_BATCH = {"block7b_u3": 16}
 
@@ -56,7 +58,12 @@ def algorithmic_bytes(f: dict, B: int = 1) -> int:
     M, K, bits = f["M"], f["K"], f["bits"]
     nnz = int(f["row_ptr"][-1])
     codes = M * K * bits // 8
-    meta = M * (K // 16) * 4 if f["fmt"] == "uniform" else M * (1 << bits) * 2
+    if f["fmt"] == "uniform":
+        meta = M * (K // 16) * 4
+    elif f["fmt"] == "bpdq":
+        meta = M * (K // f["group"]) * (bits + 1) * 2
+    else:
+        meta = M * (1 << bits) * 2
     csr = 6 * nnz + 4 * (M + 1)
     return codes + meta + csr + 2 * B * K + 4 * B * M
 

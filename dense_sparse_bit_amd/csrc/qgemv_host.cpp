@@ -182,9 +182,15 @@ int qgemv_validate_shape(const qgemv_weights* w) {
   if (!w) return QGEMV_ERR_INVALID_ARG;
   if (w->M < 1 || w->K < 1 || w->nnz < 0) return QGEMV_ERR_INVALID_ARG;
   if (w->bits != 3 && w->bits != 4) return QGEMV_ERR_UNSUPPORTED;
-  if (w->format != QGEMV_FMT_UNIFORM && w->format != QGEMV_FMT_LUT) return QGEMV_ERR_UNSUPPORTED;
+  if (w->format != QGEMV_FMT_UNIFORM && w->format != QGEMV_FMT_LUT && w->format != QGEMV_FMT_BPDQ)
+    return QGEMV_ERR_UNSUPPORTED;
   if (w->K % kChunkCodes != 0 || w->K > kMaxK) return QGEMV_ERR_UNSUPPORTED;
   if (w->format == QGEMV_FMT_UNIFORM && w->group_size != 16) return QGEMV_ERR_UNSUPPORTED;
+  if (w->format == QGEMV_FMT_BPDQ) {
+    if (w->bits != 3) return QGEMV_ERR_UNSUPPORTED;
+    if (w->group_size != 32 && w->group_size != 64 && w->group_size != 128) return QGEMV_ERR_UNSUPPORTED;
+    if (w->K % w->group_size != 0) return QGEMV_ERR_UNSUPPORTED;
+  }
   if (w->nnz > 0x1fffffffLL) return QGEMV_ERR_UNSUPPORTED;  // byte offsets of entries stay in int32
   if ((int64_t)w->M * w->K > ((int64_t)1 << 40)) return QGEMV_ERR_UNSUPPORTED;
   // the kernels address every section with 31-bit byte offsets
@@ -209,11 +215,24 @@ static int validate_arrays(const qgemv_weights* w) {
       const float z = half_to_float(w->zeros[i]);
       if (!(z >= 0.0f && z <= (float)L && z == std::floor(z))) return QGEMV_ERR_INVALID_ARG;
     }
-  } else {
+  } else if (w->format == QGEMV_FMT_LUT) {
     if (!w->lut) return QGEMV_ERR_INVALID_ARG;
     const int64_t n = M << w->bits;
     for (int64_t i = 0; i < n; ++i)
       if (!half_finite(w->lut[i])) return QGEMV_ERR_INVALID_ARG;
+  } else {
+    if (!w->coefs) return QGEMV_ERR_INVALID_ARG;
+    const int E = w->bits + 1;
+    const int64_t n = M * (K / w->group_size);
+    for (int64_t i = 0; i < n; ++i) {
+      float span = 0.0f;  // largest |level| a code can reach
+      for (int t = 0; t < E; ++t) {
+        const uint16_t c = w->coefs[i * E + t];
+        if (!half_finite(c)) return QGEMV_ERR_INVALID_ARG;
+        span += std::fabs(half_to_float(c));
+      }
+      if (span > 65504.0f) return QGEMV_ERR_UNSUPPORTED;  // levels are split into FP16 parts
+    }
   }
   if (w->row_ptr[0] != 0 || (int64_t)w->row_ptr[M] != nnz) return QGEMV_ERR_MALFORMED_CSR;
   for (int64_t i = 0; i < M; ++i) {
@@ -296,10 +315,25 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
           }
         }
       }
-  } else {
+  } else if (w->format == QGEMV_FMT_LUT) {
     const int E = 1 << bits;
     for (int i = 0; i < M; ++i)
       std::memcpy(meta + (size_t)i * h.meta_unit_bytes, w->lut + (size_t)i * E, 2 * (size_t)E);
+  } else {
+    // per (tile, K-block): [16 rows][128 / group groups][bits + 1] FP16
+    const int gs = w->group_size, gpk = kBlockK / gs, G = K / gs, E = bits + 1;
+    for (int t = 0; t < h.tiles; ++t)
+      for (int b = 0; b < nkb; ++b) {
+        uint16_t* cp = (uint16_t*)(meta + ((size_t)t * nkb + b) * h.meta_unit_bytes);
+        for (int r = 0; r < kTileRows; ++r) {
+          const int row = t * kTileRows + r;
+          for (int g = 0; g < gpk; ++g) {
+            const int gg = b * gpk + g;
+            for (int e = 0; e < E; ++e)
+              cp[(r * gpk + g) * E + e] = row < M && gg < G ? w->coefs[((size_t)row * G + gg) * E + e] : 0;
+          }
+        }
+      }
   }
 
   std::memcpy(blob + h.off_rowptr, w->row_ptr, 4ull * ((size_t)M + 1));

@@ -49,6 +49,7 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ half8_t h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4_t v = {a, b, c, d};
@@ -103,6 +104,7 @@ __device__ __forceinline__ void l3_planes(const uint32_t L[4], uint32_t t[4]) {
 template <int FMT, int BITS>
 struct Fmt {
   static constexpr bool lut = FMT == QGEMV_FMT_LUT;
+  static constexpr bool bpdq = FMT == QGEMV_FMT_BPDQ;  // 3-bit codes in the L3 placement
   static constexpr int tab_dw = lut ? (BITS == 4 ? 8 : 4) : 1;
   static constexpr int n_mfma = lut ? 4 : 8;   // per K-block, split-scale decode
 };
@@ -171,6 +173,42 @@ __device__ __forceinline__ void decode_chunk(const uint32_t (&c)[BITS], const ui
     l3_sel(c[0], c[1], c[2], sel);
 #pragma unroll
     for (int q = 0; q < 8; ++q) l3_lookup(tab, sel[q], a[q / 2][2 * (q % 2)], a[q / 2][2 * (q % 2) + 1]);
+  } else if constexpr (FMT == QGEMV_FMT_BPDQ) {
+    // st = C0 | C1 << 16, C2 | C3 << 16: the chunk's group.  The 8 levels
+    // C0 + C1 b0 + C2 b1 + C3 b2 are formed in fp32 and split into an FP16
+    // part and the FP16 rest; both tables go through the 3-bit lookups, the
+    // parts to a[0..3] and the rests to a[4..7] (two MFMAs per step).
+    const float c0 = (float)__builtin_bit_cast(_Float16, (uint16_t)st[0]);
+    const float c1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(st[0] >> 16));
+    const float c2 = (float)__builtin_bit_cast(_Float16, (uint16_t)st[1]);
+    const float c3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(st[1] >> 16));
+    float L[8];
+    L[0] = c0;
+    L[1] = c0 + c1;
+    L[2] = c0 + c2;
+    L[3] = L[1] + c2;
+    L[4] = c0 + c3;
+    L[5] = L[1] + c3;
+    L[6] = L[2] + c3;
+    L[7] = L[3] + c3;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 h0 = (_Float16)L[2 * e], h1 = (_Float16)L[2 * e + 1];
+      const _Float16 r0 = (_Float16)(L[2 * e] - (float)h0), r1 = (_Float16)(L[2 * e + 1] - (float)h1);
+      hi[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lo[e] = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+    }
+    uint32_t th[4], tl[4];
+    l3_planes(hi, th);
+    l3_planes(lo, tl);
+    uint32_t sel[8];
+    l3_sel(c[0], c[1], c[2], sel);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      l3_lookup(th, sel[q], a[q / 2][2 * (q % 2)], a[q / 2][2 * (q % 2) + 1]);
+      l3_lookup(tl, sel[q], a[4 + q / 2][2 * (q % 2)], a[4 + q / 2][2 * (q % 2) + 1]);
+    }
   } else {
     uint32_t qz[16], shi[2], slo[2];
     uniform_qz<BITS>(c, (st[0] >> 16) | (st[1] & 0xFFFF0000u), qz);
@@ -286,7 +324,7 @@ __global__ void __launch_bounds__(64 * kWaves)
 k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
          const uint32_t* __restrict__ entries, const int32_t* __restrict__ boff, const uint32_t* __restrict__ bent,
          const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K, int Kp, int nkb, int tiles,
-         uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap) {
+         uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap, int gsz) {
   using F = Fmt<FMT, BITS>;
   constexpr int BB = 256 * BITS;
   constexpr bool B1 = NB == 1;
@@ -354,12 +392,16 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   // Uniform statistics of a K-block (see qgemv_layout.h): the z pair of the
   // lane's two groups, and either the s pair (split-scale decode, batch NB) or
   // the scales of group lane % 16 for rows 4*(lane/16) .. +3 (batch 1).
-  constexpr bool UG1 = B1 && !F::lut;  // batch-1 uniform: MFMA columns are the K-block's groups
+  constexpr bool UG1 = B1 && FMT == QGEMV_FMT_UNIFORM;  // batch-1 uniform: MFMA columns are the K-block's groups
   constexpr int SBW = UG1 ? 5 : 2;
   const uint32_t zoff = (uint32_t)(lane & 15) * 16 + (uint32_t)(lane >> 4) * 4;
   const uint32_t spoff = 256 + (uint32_t)(lane >> 4) * 64 + (uint32_t)(lane & 15) * 4;
   const uint32_t sqoff = (lane & 15) < 8 ? 256 + (uint32_t)((lane & 15) >> 1) * 64 + (uint32_t)(lane >> 4) * 16
                                          : kOutOfRange;
+  // BPDQ coefficients of a K-block: [16 rows][128/gsz groups][4] FP16; lane
+  // (row lane % 16, columns 32*(lane/16) .. +31) takes its group's 8 bytes.
+  const uint32_t cunit = 16384u / (uint32_t)gsz;
+  const uint32_t coff = ((uint32_t)(lane & 15) * (128u / (uint32_t)gsz) + (uint32_t)(32 * (lane >> 4)) / (uint32_t)gsz) * 8u;
   // What goes to LDS is loaded first: the x slice (batch 1), the row_ptr
   // slice and the tables, at most 2 + 1 + 1 pieces per thread.  The code
   // ring is issued right behind, so storing the staged pieces waits for them
@@ -420,7 +462,12 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   auto issue = [&](int u, int g) {  // g: blob block index, -1 for none
     const bool in = g >= 0;
     load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
-    if constexpr (!F::lut) {
+    if constexpr (F::bpdq) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(in ? (uint32_t)g * cunit + coff : kOutOfRange),
+                                                             0, kNonTemporal);
+      sb[u][0] = v[0];
+      sb[u][1] = v[1];
+    } else if constexpr (!F::lut) {
       const uint32_t mb = in ? (uint32_t)g * 512 : kOutOfRange;
       sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? mb + zoff : kOutOfRange), 0, kNonTemporal);
       if constexpr (UG1) {
@@ -581,7 +628,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
             }
           } else {
             uint32_t am[F::n_mfma][4];
-            if constexpr (F::lut) {
+            if constexpr (F::lut || F::bpdq) {
               decode_chunk<FMT, BITS>(cb[sl], sb[sl], tab, am);
             } else {
               const uint32_t st[2] = {perm(sb[sl][0], sb[sl][1], 0x05040100u),
@@ -747,7 +794,7 @@ template <int FMT, int BITS, int NB, int R>
 __global__ void __launch_bounds__(64 * kWaves)
 k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
        const uint32_t* __restrict__ entries, const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K,
-       int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap) {
+       int Kp, int nkb, int tiles, uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int ent_cap, int gsz) {
   using F = Fmt<FMT, BITS>;
   constexpr int BB = 256 * BITS;
   constexpr int NP = NB / 2;
@@ -819,13 +866,20 @@ k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   const uint32_t voff = (uint32_t)lane * 4 * BITS;
   const uint32_t zoff = (uint32_t)(lane & 15) * 16 + (uint32_t)(lane >> 4) * 4;
   const uint32_t spoff = 256 + (uint32_t)(lane >> 4) * 64 + (uint32_t)(lane & 15) * 4;
+  const uint32_t cunit = 16384u / (uint32_t)gsz;  // BPDQ coefficients, as in k_stream
+  const uint32_t coff = ((uint32_t)(lane & 15) * (128u / (uint32_t)gsz) + (uint32_t)(32 * (lane >> 4)) / (uint32_t)gsz) * 8u;
   uint32_t cb[R][BITS];
   uint32_t sb[R][2];
   auto issue = [&](int u, int b) {  // b: block of the workgroup, -1 for none
     const bool in = b >= 0;
     const uint32_t g = (uint32_t)(T0 * nkb + b);
     load_chunk<BITS>(cb[u], rc, in ? g * BB + voff : kOutOfRange);
-    if constexpr (!F::lut) {
+    if constexpr (F::bpdq) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(in ? g * cunit + coff : kOutOfRange), 0,
+                                                             kNonTemporal);
+      sb[u][0] = v[0];
+      sb[u][1] = v[1];
+    } else if constexpr (!F::lut) {
       sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? g * 512 + zoff : kOutOfRange), 0, kNonTemporal);
       sb[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? g * 512 + spoff : kOutOfRange), 0, kNonTemporal);
     } else {
@@ -886,7 +940,7 @@ k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
           planes();
         }
         uint32_t am[F::n_mfma][4];
-        if constexpr (F::lut) {
+        if constexpr (F::lut || F::bpdq) {
           decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
         } else {
           const uint32_t st[2] = {perm(sb[u][0], sb[u][1], 0x05040100u), perm(sb[u][0], sb[u][1], 0x07060302u)};
@@ -1331,7 +1385,7 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
                      (const uint32_t*)(p->blob + h.off_entries), (const int32_t*)(p->blob + h.off_boff),
                      (const uint32_t*)(p->blob + h.off_bent), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
-                     meta_bytes, (int)h.nnz, (int)(cap / 4));
+                     meta_bytes, (int)h.nnz, (int)(cap / 4), h.group_size > 0 ? h.group_size : 16);
   return hipGetLastError();
 }
 
@@ -1378,7 +1432,7 @@ hipError_t launch_xlds(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   hipLaunchKernelGGL((k_xlds<FMT, BITS, NB, R>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
                      (const uint32_t*)(p->blob + h.off_entries), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
-                     meta_bytes, (int)h.nnz, (int)(cap / 4));
+                     meta_bytes, (int)h.nnz, (int)(cap / 4), h.group_size > 0 ? h.group_size : 16);
   return hipGetLastError();
 }
 
@@ -1479,6 +1533,8 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
   hipError_t e;
   if (h->h.format == QGEMV_FMT_LUT)
     e = b4 ? launch_run<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_run<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
+  else if (h->h.format == QGEMV_FMT_BPDQ)
+    e = launch_run<QGEMV_FMT_BPDQ, 3>(h, x, y_dev, batch, st);
   else
     e = b4 ? launch_run<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, batch, st)
            : launch_run<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, batch, st);
@@ -1490,7 +1546,7 @@ int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream) {
   if ((uintptr_t)codes_dev % 16) return QGEMV_ERR_INVALID_ARG;
   const hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (h->h.format == QGEMV_FMT_LUT)
+  if (h->h.format == QGEMV_FMT_LUT || h->h.format == QGEMV_FMT_BPDQ)  // BPDQ codes use the L3 placement
     e = h->h.bits == 4 ? launch_unpack<QGEMV_FMT_LUT, 4>(h, codes_dev, st)
                        : launch_unpack<QGEMV_FMT_LUT, 3>(h, codes_dev, st);
   else

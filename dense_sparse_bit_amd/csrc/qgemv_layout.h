@@ -36,7 +36,12 @@
 //      bits of code 24+k, of dword 1 the low bits of code 28+k; bit 6 (7) of
 //      byte k of dword 2 is bit 2 of code 24+k (28+k).
 //
+//   BPDQ codes (3 bit) use the L3 placement.
+//
 // meta    LUT: per row (tiles*16 rows) the canonical FP16 table, 2^bits entries.
+//         BPDQ: per (tile, K-block) the FP16 coefficients [16 rows][128/group
+//         groups][bits + 1] (C0 first); a lane's chunk lies in one group, whose
+//         coefficients are one 8-byte piece.
 //         UNIFORM: 512 bytes per (tile, K-block) for its 16 rows x 8 groups of
 //         16 codes: a z plane, FP16 zero points [row][group] (256 B), then an
 //         s plane, FP16 scales [group / 2][row][group % 2] (256 B).  Lane l's
@@ -92,16 +97,18 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
   h.K = K;
   h.bits = bits;
   h.format = format;
-  h.group_size = format == 0 ? group : 0;
+  h.group_size = format == 1 ? 0 : group;
   h.tiles = (M + kTileRows - 1) / kTileRows;
   h.nnz = nnz;
   h.Kp = (K + kBlockK - 1) / kBlockK * kBlockK;
   h.nkb = h.Kp / kBlockK;
   h.block_bytes = (uint32_t)(64 * 4 * bits);
-  h.meta_unit_bytes = format == 0 ? 64u * 8u : (uint32_t)(2u << bits);
+  h.meta_unit_bytes = format == 0   ? 64u * 8u
+                      : format == 1 ? (uint32_t)(2u << bits)
+                                    : (uint32_t)(kTileRows * (kBlockK / (group > 0 ? group : kBlockK)) * (bits + 1) * 2);
   const uint64_t nblocks = (uint64_t)h.tiles * h.nkb;
   const uint64_t meta_bytes =
-      format == 0 ? nblocks * h.meta_unit_bytes : (uint64_t)h.tiles * kTileRows * h.meta_unit_bytes;
+      format == 1 ? (uint64_t)h.tiles * kTileRows * h.meta_unit_bytes : nblocks * h.meta_unit_bytes;
   h.off_codes = kHeaderBytes;
   h.off_meta = align_up(h.off_codes + nblocks * h.block_bytes);
   h.off_rowptr = align_up(h.off_meta + meta_bytes);

@@ -6,9 +6,10 @@ If the shared library is missing this module raises instead of falling back
 to anything else.
 
 Canonical arrays are passed as a dict with the keys of the C struct
-``qgemv_weights``: M, K, bits, fmt ("uniform" | "lut"), group, codes_packed
-(uint8 [M, K*bits/8]), scales / zeros (FP16 [M, K/16]) or lut (FP16
-[M, 2^bits]), row_ptr (int32 [M+1]), col_idx (int32 [nnz]), values (FP16 [nnz]).
+``qgemv_weights``: M, K, bits, fmt ("uniform" | "lut" | "bpdq"), group,
+codes_packed (uint8 [M, K*bits/8]), scales / zeros (FP16 [M, K/16]), lut (FP16
+[M, 2^bits]) or coefs (FP16 [M, K/group, bits+1]), row_ptr (int32 [M+1]),
+col_idx (int32 [nnz]), values (FP16 [nnz]).
 """
 
 from __future__ import annotations
@@ -23,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsb_qgemv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qgemv.h")
 
-FMT = {"uniform": 0, "lut": 1}
+FMT = {"uniform": 0, "lut": 1, "bpdq": 2}
 STATUS = {0: "QGEMV_OK", -1: "QGEMV_ERR_INVALID_ARG", -2: "QGEMV_ERR_MALFORMED_CSR",
           -3: "QGEMV_ERR_UNSUPPORTED", -4: "QGEMV_ERR_HIP", -5: "QGEMV_ERR_SIZE"}
 
@@ -40,7 +41,7 @@ class Weights(ctypes.Structure):
         ("format", ctypes.c_int32), ("group_size", ctypes.c_int32), ("nnz", ctypes.c_int64),
         ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
         ("lut", ctypes.c_void_p), ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
-        ("values", ctypes.c_void_p),
+        ("values", ctypes.c_void_p), ("coefs", ctypes.c_void_p),
     ]
 
 
@@ -113,6 +114,7 @@ def make_weights(w: dict):
     s.row_ptr = ptr(row_ptr, np.int32)
     s.col_idx = ptr(w.get("col_idx"), np.int32) if nnz else None
     s.values = ptr(w.get("values"), np.uint16) if nnz else None
+    s.coefs = ptr(w.get("coefs"), np.uint16)
     return s, keep
 
 

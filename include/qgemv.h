@@ -13,7 +13,10 @@
  * 2^bits entries (SqueezeLLM page, section "Non-uniform quantization via
  * Lloyd-Max optimisé").  The sparse part holds FP16 outliers in CSR form
  * (SpQR page, section "Le format de stockage sparse": values FP16, col_idx,
- * row_ptr).
+ * row_ptr).  A third dense decode, QGEMV_FMT_BPDQ, follows the page "BPDQ:
+ * Bit-Plane Decomposition Quantization on a Variable Grid for Large Language
+ * Models", section "1. Formulation de la Grille Variable": the code's bit
+ * planes select per-group FP16 coefficients, d = C0 + sum_t C_t * B_t.
  *
  * Flow: qgemv_packed_size + qgemv_repack (host, offline) turn the canonical
  * arrays below into one self-describing blob laid out for the gfx950 kernels;
@@ -50,7 +53,9 @@ typedef enum {
 
 typedef enum {
   QGEMV_FMT_UNIFORM = 0, /* d = scale[i][g] * (q - zero[i][g]),  g = j / group_size */
-  QGEMV_FMT_LUT = 1      /* d = lut[i][q]                                            */
+  QGEMV_FMT_LUT = 1,     /* d = lut[i][q]                                            */
+  QGEMV_FMT_BPDQ = 2     /* d = coefs[i][g][0] + sum_{t=1..bits} coefs[i][g][t] *
+                            ((q >> (t-1)) & 1),  g = j / group_size                  */
 } qgemv_format;
 
 /*
@@ -58,9 +63,10 @@ typedef enum {
  * little-endian, row-major, borrowed for the duration of the call only.
  *
  *   M, K        W is M x K (out x in).  K % 32 == 0, 32 <= K <= 16384, M >= 1.
- *   bits        3 or 4.
+ *   bits        3 or 4 (BPDQ: 3).
  *   format      qgemv_format.
- *   group_size  16 for QGEMV_FMT_UNIFORM (groups run along K); ignored for LUT.
+ *   group_size  groups run along K.  16 for QGEMV_FMT_UNIFORM; 32, 64 or 128
+ *               for QGEMV_FMT_BPDQ, with K % group_size == 0; ignored for LUT.
  *   nnz         number of CSR entries, >= 0.
  *   codes       uint8 [M][K*bits/8]: row i is one contiguous bitstream starting
  *               at byte i*K*bits/8; code j occupies bits [j*bits, j*bits+bits),
@@ -69,6 +75,9 @@ typedef enum {
  *   zeros       FP16 bits [M][K/group_size] (UNIFORM), else NULL.  Integer
  *               valued in [0, 2^bits - 1].
  *   lut         FP16 bits [M][2^bits] (LUT), else NULL.  Finite.
+ *   coefs       FP16 bits [M][K/group_size][bits+1] (BPDQ), else NULL: the
+ *               group's C0, then C1 .. C_bits (plane t = bit t-1 of the code).
+ *               Finite.
  *   row_ptr     int32 [M+1]: row_ptr[0] = 0, non-decreasing, row_ptr[M] = nnz.
  *   col_idx     int32 [nnz]: 0 <= c < K, strictly ascending inside a row.
  *   values      FP16 bits [nnz], finite.  col_idx/values may be NULL iff nnz == 0.
@@ -86,6 +95,7 @@ typedef struct {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const uint16_t* values;
+  const uint16_t* coefs;
 } qgemv_weights;
 
 typedef struct qgemv_plan* qgemv_handle;

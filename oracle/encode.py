@@ -9,6 +9,7 @@ Step order follows the pages:
   2. dense part with holes, quantized  [SpQR] "La solution SpQR : décomposition sparse + dense",
                                               "Quantification d'un modèle" (wbits, groupsize 16)
                                        [SqLLM] "Non-uniform quantization via Lloyd-Max optimisé"
+                                       [BPDQ] "Formulation de la Grille Variable", "Cadre d'Optimisation"
   3. sparse residual in CSR            [SpQR] "Le format de stockage sparse"
                                        [SqLLM] "2. Dense-and-Sparse decomposition" (W = W_dense + W_sparse)
 
@@ -200,6 +201,121 @@ def ssqr_alpha(W16: np.ndarray, bits: int, group: int, n: int, iters: int = 40) 
 
 
 # --------------------------------------------------------------------------
+# 2c. BPDQ: bit planes on a variable grid
+# --------------------------------------------------------------------------
+def bpdq_levels(c: np.ndarray, k: int) -> np.ndarray:
+    """The 2^k values of one group's grid: level(q) = C0 + sum_i C_i * bit_(i-1)(q).
+
+    [BPDQ] "1. Formulation de la Grille Variable": W^ = REP(C0) + sum_i REP(C_i) (.) B_i
+    with B_i in {0, 1}.  Reading: plane B_i of a weight is bit i-1 of its
+    k-bit code (plane 1 the least significant).
+    """
+    q = np.arange(1 << k)
+    lv = np.full(q.size, float(c[0]))
+    for i in range(1, k + 1):
+        lv = lv + float(c[i]) * ((q >> (i - 1)) & 1)
+    return lv
+
+
+def bpd_init(w: np.ndarray, k: int) -> np.ndarray:
+    """Initial codes: the k most significant bit planes of the weights.
+
+    [BPDQ] "2. Cadre d'Optimisation", initialisation: the planes come from the
+    bit-plane decomposition of the weights, keeping the k most significant.
+    Reading: a group's weights are mapped onto [0, 1] by its min and max; the
+    code is the fraction's binary expansion cut to k bits,
+    q = min(floor(2^k u), 2^k - 1) (all 0 if the group is constant).
+    """
+    lo, hi = float(w.min()), float(w.max())
+    if hi == lo:
+        return np.zeros(w.size, dtype=np.int64)
+    u = (w - lo) / (hi - lo)
+    return np.minimum(np.floor(u * (1 << k)), (1 << k) - 1).astype(np.int64)
+
+
+def bpdq_fit(w: np.ndarray, q: np.ndarray, k: int) -> np.ndarray:
+    """Coefficients (C0 .. Ck) minimising sum (w - level(q))^2, in fp64.
+
+    [BPDQ] "2. Cadre d'Optimisation": scalar coefficients by an analytic
+    least-squares fit.  Reading: no calibration data here, so the Hessian
+    metric is the identity and the fit is ordinary least squares on the design
+    [1, B_1 .. B_k]; numpy's lstsq gives the minimum-norm solution when a plane
+    is constant over the group.
+    """
+    A = np.stack([np.ones(w.size)] + [((q >> (i - 1)) & 1).astype(np.float64) for i in range(1, k + 1)], axis=1)
+    return np.linalg.lstsq(A, w, rcond=None)[0]
+
+
+def bpdq_assign(w: np.ndarray, c: np.ndarray, k: int) -> np.ndarray:
+    """Codes by exact enumeration of the 2^k bit patterns (ties: lower code).
+
+    [BPDQ] "2. Cadre d'Optimisation", refinement step 1: for fixed
+    coefficients the bit planes are updated by exact enumeration.  Reading:
+    with the identity metric every weight is independent, so each takes the
+    pattern whose level is nearest.
+    """
+    return nearest(w, bpdq_levels(c, k)).astype(np.int64)
+
+
+def bpdq_group(w: np.ndarray, k: int, max_iter: int = 20, history: list | None = None):
+    """One group: BPD initialisation, then alternate refits and bit updates.
+
+    [BPDQ] "2. Cadre d'Optimisation": initialise the planes by BPD, fit the
+    coefficients, then alternate (1) bit updates by enumeration and (2)
+    least-squares refits.  Readings: stop when the codes no longer change or
+    after max_iter rounds; the coefficients are then rounded to FP16 (the
+    stored format) and the codes chosen once more against the rounded values.
+    No delta correction: with the identity metric no error is propagated to
+    other columns.
+    Returns (codes int64, FP16 coefficients as fp64 [k+1]).
+    If `history` is a list, the objective after every refit is appended.
+    """
+    if w.size == 0:
+        return np.zeros(0, dtype=np.int64), np.zeros(k + 1)
+    q = bpd_init(w, k)
+    for _ in range(max_iter):
+        c = bpdq_fit(w, q, k)
+        if history is not None:
+            history.append(float(np.sum((w - bpdq_levels(c, k)[q]) ** 2)))
+        q2 = bpdq_assign(w, c, k)
+        if np.array_equal(q2, q):
+            break
+        q = q2
+    c16 = f16(bpdq_fit(w, q, k))
+    return bpdq_assign(w, c16, k), c16
+
+
+def quant_bpdq(W16: np.ndarray, hole: np.ndarray, bits: int, group: int):
+    """BPDQ dense part: per (row, group of `group` columns) FP16 coefficients and k-bit codes.
+
+    The fit uses the group's non-outlier weights.  At an outlier position the
+    code is the one whose level is nearest 0 (ties: lower code); the CSR then
+    holds the residual fp16(w - level) (build_csr), so W_dense + W_sparse
+    reproduces the outlier to FP16 rounding of the residual.
+
+    Returns (codes uint8 [M, K], coefs fp16 [M, K/group, bits+1]).
+    """
+    M, K = W16.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    W = W16.astype(np.float64)
+    codes = np.zeros((M, K), dtype=np.uint8)
+    coefs = np.zeros((M, G, bits + 1), dtype=np.float16)
+    for i in range(M):
+        for g in range(G):
+            sl = slice(g * group, (g + 1) * group)
+            w, h = W[i, sl], hole[i, sl]
+            q = np.zeros(group, dtype=np.int64)
+            qk, c = bpdq_group(w[~h], bits)
+            q[~h] = qk
+            q[h] = int(np.argmin(np.abs(bpdq_levels(c, bits))))
+            codes[i, sl] = q
+            coefs[i, g] = c.astype(np.float16)
+    return codes, coefs
+
+
+# --------------------------------------------------------------------------
 # 2b. Sensitivity-weighted Lloyd-Max LUT (non-uniform)
 # --------------------------------------------------------------------------
 def weighted_quantile(w: np.ndarray, s: np.ndarray, qs) -> np.ndarray:
@@ -375,6 +491,9 @@ def encode(W16: np.ndarray, bits: int, fmt: str, n_outliers: int, group: int = 1
             raise ValueError("LUT quantization needs a sensitivity vector")
         codes, lut = quant_lut(W16, hole, np.asarray(sens, dtype=np.float64), bits)
         out.update(lut=lut)
+    elif fmt == "bpdq":
+        codes, coefs = quant_bpdq(W16, hole, bits, group)
+        out.update(coefs=coefs, group=group)
     else:
         raise ValueError(fmt)
     out["codes"] = codes

@@ -24,6 +24,8 @@ def decode_rows(enc: dict, rows=None, codes: np.ndarray | None = None) -> np.nda
         d_ij = scale_{i,g(j)} * (q_ij - zero_{i,g(j)}),  g(j) = j // group
     LUT ([SqLLM] "Non-uniform quantization via Lloyd-Max optimisé"):
         d_ij = LUT_i[q_ij]
+    BPDQ ([BPDQ] "1. Formulation de la Grille Variable"):
+        d_ij = C0 + sum_t C_t * bit_(t-1)(q_ij), coefficients of (row i, group j // group)
     Codes are read from the packed bitstream unless given.
     """
     M, K, bits = enc["M"], enc["K"], enc["bits"]
@@ -39,6 +41,16 @@ def decode_rows(enc: dict, rows=None, codes: np.ndarray | None = None) -> np.nda
     if enc["fmt"] == "lut":
         lut = np.asarray(enc["lut"])[rows].astype(np.float64)
         return np.take_along_axis(lut, codes.astype(np.int64), axis=1)
+    if enc["fmt"] == "bpdq":
+        # [BPDQ] "1. Formulation de la Grille Variable": d = C0 + sum_i C_i * B_i,
+        # coefficients per (row, group), plane i = bit i-1 of the code.
+        g = enc["group"]
+        C = np.repeat(np.asarray(enc["coefs"])[rows].astype(np.float64), g, axis=1)  # [R, K, bits+1]
+        c = codes.astype(np.int64)
+        d = C[:, :, 0].copy()
+        for i in range(1, bits + 1):
+            d += C[:, :, i] * ((c >> (i - 1)) & 1)
+        return d
     raise ValueError(enc["fmt"])
 
 

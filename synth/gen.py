@@ -33,8 +33,8 @@ class Workload:
     M: int              # output rows (out features)
     K: int              # input columns (in features)
     bits: int           # code width
-    fmt: str            # "uniform" (group scale/zero) or "lut" (per-row table)
-    group: int          # group size along K for "uniform", 0 for "lut"
+    fmt: str            # "uniform" (group scale/zero), "lut" (per-row table) or "bpdq" (bit-plane coefficients)
+    group: int          # group size along K for "uniform" and "bpdq", 0 for "lut"
     density: float      # outlier fraction of M*K
     sigma: float        # std of the Gaussian bulk
     law: str            # outlier placement law (see make_weights)
@@ -65,6 +65,10 @@ WORKLOADS = {
         4096, 4096, 3, "uniform", 16, 0.01, 0.02, "uniform_pos", (16,),
         (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
          ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008))),
+    "mlp7b_bpdq3": Workload(
+        6, "mlp7b_bpdq3",
+        "MLP up-proj 11008x4096, 3-bit BPDQ variable grid (4 FP16 coefficients per row and group of 64), 0.45% outliers",
+        11008, 4096, 3, "bpdq", 64, 0.0045, 0.02, "uniform_pos", (1, 8)),
 }
 
 
@@ -203,6 +207,8 @@ def make_format_inputs(wl: Workload | str, layer: int = 0, M: int | None = None,
     Codes are uniformly random bytes (every bit pattern of the per-row
     bitstream is a valid sequence of b-bit codes).  Uniform workloads get
     positive FP16 scales and integer-valued FP16 zero points in [0, 2^b - 1];
+    BPDQ workloads get per-group coefficients C0 ~ -U(3, 4) sigma and
+    C_t ~ U(0.5, 1.5) 2^(t-1) sigma;
     LUT workloads get one ascending FP16 table per row holding an exact 0.0
     and 2^b - 1 Gaussian draws.  Outlier positions follow the workload's
     placement law (value-ranked laws are drawn uniformly, which gives the same
@@ -222,6 +228,13 @@ def make_format_inputs(wl: Workload | str, layer: int = 0, M: int | None = None,
         G = K // wl.group
         out["scales"] = (rng.uniform(0.5, 1.5, size=(M, G)) * 4 * wl.sigma / (levels - 1)).astype(np.float16)
         out["zeros"] = rng.integers(0, levels, size=(M, G)).astype(np.float16)
+    elif wl.fmt == "bpdq":
+        G = K // wl.group
+        c = np.empty((M, G, wl.bits + 1))
+        c[:, :, 0] = -rng.uniform(3.0, 4.0, size=(M, G)) * wl.sigma
+        for t in range(1, wl.bits + 1):
+            c[:, :, t] = rng.uniform(0.5, 1.5, size=(M, G)) * (1 << (t - 1)) * wl.sigma
+        out["coefs"] = c.astype(np.float16)
     else:
         draws = rng.standard_normal((M, levels - 1)) * 2 * wl.sigma
         lut = np.concatenate([draws, np.zeros((M, 1))], axis=1).astype(np.float16)

@@ -31,14 +31,17 @@ def test_error_strings():
     assert L.qgemv_last_hip_error() == 0
 
 
-def _random_canonical(fmt, bits, M, K, nnz_per_row=3, seed=0):
+def _random_canonical(fmt, bits, M, K, nnz_per_row=3, seed=0, group=32):
     rng = np.random.default_rng(seed)
     codes = rng.integers(0, 1 << bits, size=(M, K)).astype(np.uint8)
-    w = {"M": M, "K": K, "bits": bits, "fmt": fmt, "group": 16 if fmt == "uniform" else 0,
+    w = {"M": M, "K": K, "bits": bits, "fmt": fmt,
+         "group": 16 if fmt == "uniform" else group if fmt == "bpdq" else 0,
          "codes": codes, "codes_packed": pack.pack_bitstream(codes, bits)}
     if fmt == "uniform":
         w["scales"] = rng.uniform(1e-3, 2e-2, size=(M, K // 16)).astype(np.float16)
         w["zeros"] = rng.integers(0, 1 << bits, size=(M, K // 16)).astype(np.float16)
+    elif fmt == "bpdq":
+        w["coefs"] = (rng.standard_normal((M, K // group, bits + 1)) * 0.03).astype(np.float16)
     else:
         w["lut"] = np.sort(rng.standard_normal((M, 1 << bits)) * 0.05, axis=1).astype(np.float16)
     cols = [np.sort(rng.choice(K, size=min(K, nnz_per_row), replace=False)) for _ in range(M)]
@@ -48,7 +51,7 @@ def _random_canonical(fmt, bits, M, K, nnz_per_row=3, seed=0):
     return w
 
 
-FORMATS = [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4)]
+FORMATS = [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4), ("bpdq", 3)]
 
 
 @pytest.mark.parametrize("fmt,bits", FORMATS)
@@ -72,13 +75,15 @@ def test_repack_roundtrip_every_code_value_in_every_slot(fmt, bits):
 
 
 @pytest.mark.parametrize("name,M,K", [("tiny_u4", None, None), ("attn7b_u3", 40, 2080),
-                                      ("mlp7b_lut3", 12, 4096), ("mlp70b_lut4", 6, 4128)])
+                                      ("mlp7b_lut3", 12, 4096), ("mlp70b_lut4", 6, 4128),
+                                      ("mlp7b_bpdq3", 20, 1024)])
 def test_repack_roundtrip_oracle_encoding(name, M, K):
     wl = WORKLOADS[name]
     W, planted = make_weights(wl, 0, M, K)
     M, K = W.shape
     x = make_x(wl, 1, K, 0, M)
-    enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M, K), 16, sens=x[0].astype(np.float64) ** 2)
+    enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M, K), wl.group or 16,
+                        sens=x[0].astype(np.float64) ** 2)
     blob = qgemv.repack(enc)
     assert np.array_equal(qgemv.unpack_host(blob, M, K), enc["codes"])
     # header, row_ptr and entries sections
@@ -202,3 +207,42 @@ def test_run_and_create_argument_checks_need_no_gpu():
     assert L.qgemv_create(ctypes.byref(h), ctypes.byref(s), ctypes.c_void_p(0x1001), 1 << 20) == -1
     # a blob smaller than the descriptor needs is rejected before any HIP call
     assert L.qgemv_create(ctypes.byref(h), ctypes.byref(s), ctypes.c_void_p(0x100000), 256) == -5
+
+
+
+@pytest.mark.parametrize("group,K", [(32, 4128), (64, 4096), (128, 384), (64, 1088)])
+def test_bpdq_coefficients_in_blob(group, K):
+    """Per (tile, K-block) the blob holds [16 rows][128/group][4] FP16 coefficients,
+    zero for padding rows and for groups past K."""
+    M = 21
+    w = _random_canonical("bpdq", 3, M, K, group=group, seed=group)
+    blob = qgemv.repack(w)
+    off = blob[:256].view(np.uint64)
+    off_meta = int(off[6])  # header: magic/version, M/K, bits/format, group/tiles, nnz, off_codes, off_meta
+    tiles, nkb, gpk = (M + 15) // 16, (K + 127) // 128, 128 // group
+    meta = blob[off_meta:off_meta + tiles * nkb * 16 * gpk * 8].view(np.uint16).reshape(tiles, nkb, 16, gpk, 4)
+    want = np.zeros((tiles * 16, nkb * gpk, 4), dtype=np.uint16)
+    want[:M, :K // group] = w["coefs"].view(np.uint16)
+    want = want.reshape(tiles, 16, nkb, gpk, 4).transpose(0, 2, 1, 3, 4)
+    assert np.array_equal(meta, want)
+
+
+def test_bpdq_validation():
+    INV, UNS = -1, -3
+    base = _random_canonical("bpdq", 3, 4, 256, group=64)
+    assert _status(base) == 0
+    for bad in ({"bits": 4}, {"group": 16}, {"group": 48}):
+        w = dict(base); w.update(bad)
+        if "bits" in bad:
+            w["codes"] = np.zeros((4, 256), np.uint8); w["codes_packed"] = pack.pack_bitstream(w["codes"], 4)
+        assert _status(w) == UNS, bad
+    w = _random_canonical("bpdq", 3, 4, 96, group=64)  # K % group != 0
+    assert _status(w) == UNS
+    w = dict(base); w["coefs"] = None
+    assert _status(w) == INV
+    c = base["coefs"].copy(); c[1, 2, 3] = np.nan
+    w = dict(base); w["coefs"] = c
+    assert _status(w) == INV
+    c = base["coefs"].copy(); c[0, 0] = [40000.0, 30000.0, 0.0, 0.0]  # a level beyond FP16 range
+    w = dict(base); w["coefs"] = c
+    assert _status(w) == UNS

@@ -55,7 +55,7 @@ def oracle_case(name, M, K, layer=0):
         W, planted = make_weights(wl, layer, M, K)
         M_, K_ = W.shape
         x = make_x(wl, max(wl.batches), K_, layer, M_)
-        enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M_, K_), 16,
+        enc = encode.encode(W, wl.bits, wl.fmt, outlier_count(wl, M_, K_), wl.group or 16,
                             sens=x[0].astype(np.float64) ** 2)
         _ENC[key] = (enc, x)
     return _ENC[key]
@@ -96,6 +96,8 @@ SMALL_CASES = [
     ("mlp70b_lut4", 24, 8192),        # 2 full outlier columns + heavy rows
     ("mlp70b_lut4", 40, 2080),
     ("block7b_u3", 96, 11008),        # down-proj K: 5 full steps + a 24-lane tail
+    ("mlp7b_bpdq3", 64, 4096),        # BPDQ: 4 coefficients per row and group of 64
+    ("mlp7b_bpdq3", 33, 2112),        # ragged M, a K-block half past K
 ]
 
 
@@ -152,7 +154,7 @@ def test_small_ssqr(torch, name, M, K, budget):
 
 FULL_CASES = [
     ("tiny_u4", 0), ("attn7b_u3", 0), ("mlp7b_lut3", 0), ("mlp70b_lut4", 0),
-    ("block7b_u3", 0), ("block7b_u3", 4), ("block7b_u3", 6),
+    ("block7b_u3", 0), ("block7b_u3", 4), ("block7b_u3", 6), ("mlp7b_bpdq3", 0),
 ]
 
 
@@ -186,6 +188,9 @@ def _custom(fmt, bits, M, K, row_nnz, seed=0):
     if fmt == "uniform":
         f["scales"] = rng.uniform(1e-3, 3e-2, size=(M, K // 16)).astype(np.float16)
         f["zeros"] = rng.integers(0, 1 << bits, size=(M, K // 16)).astype(np.float16)
+    elif fmt == "bpdq":
+        f["group"] = 32
+        f["coefs"] = (rng.standard_normal((M, K // 32, bits + 1)) * 0.03).astype(np.float16)
     else:
         f["lut"] = np.sort(rng.standard_normal((M, 1 << bits)) * 0.05, axis=1).astype(np.float16)
     rows, cols = [], []
@@ -199,7 +204,7 @@ def _custom(fmt, bits, M, K, row_nnz, seed=0):
     return f
 
 
-@pytest.mark.parametrize("fmt,bits", [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4)])
+@pytest.mark.parametrize("fmt,bits", [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4), ("bpdq", 3)])
 def test_edge_cases(torch, fmt, bits):
     cases = {
         "no_outliers": _custom(fmt, bits, 70, 2048, [0] * 70, seed=1),
@@ -227,7 +232,7 @@ def _rows_of(f, rng, extra=()):
     return np.unique(np.concatenate([[0, 1, M - 2, M - 1], heavy, pick, np.asarray(extra, np.int64)]))
 
 
-@pytest.mark.parametrize("fmt,bits", [("lut", 4), ("lut", 3), ("uniform", 3), ("uniform", 4)])
+@pytest.mark.parametrize("fmt,bits", [("lut", 4), ("lut", 3), ("uniform", 3), ("uniform", 4), ("bpdq", 3)])
 @pytest.mark.parametrize("label,M,K,heavy", [
     ("tw8_ragged", 32768 - 5, 256, 0),      # 8 tiles per workgroup (two LUT-4 table regions), short last tile
     ("tw5", 16 * 256 * 5 - 3, 384, 0),      # 5 tiles: the second LUT-4 region holds one tile
@@ -302,6 +307,8 @@ BATCHED_SMALL = [
     ("mlp70b_lut4", 24, 8192, 8),
     ("mlp70b_lut4", 40, 2080, 16),
     ("block7b_u3", 96, 11008, 16),
+    ("mlp7b_bpdq3", 64, 4096, 8),
+    ("mlp7b_bpdq3", 33, 2112, 16),
 ]
 
 
@@ -320,7 +327,7 @@ def test_batched_oracle_encoded(torch, name, M, K, B):
 
 
 @pytest.mark.parametrize("name,layer,B", [("mlp70b_lut4", 0, 8), ("block7b_u3", 0, 16), ("block7b_u3", 4, 16),
-                                          ("block7b_u3", 6, 16)])
+                                          ("block7b_u3", 6, 16), ("mlp7b_bpdq3", 0, 8)])
 def test_batched_full_size_sampled(torch, name, layer, B):
     f = format_case(name, layer)
     M, K = f["M"], f["K"]
@@ -337,7 +344,7 @@ def test_batched_full_size_sampled(torch, name, layer, B):
     plan.close()
 
 
-@pytest.mark.parametrize("fmt,bits", [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4)])
+@pytest.mark.parametrize("fmt,bits", [("uniform", 3), ("uniform", 4), ("lut", 3), ("lut", 4), ("bpdq", 3)])
 @pytest.mark.parametrize("B", [8, 16])
 def test_batched_edge_cases(torch, fmt, bits, B):
     cases = {

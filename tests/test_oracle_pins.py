@@ -164,6 +164,12 @@ def brute_force_y(enc, X16):
                 if enc["fmt"] == "uniform":
                     g = j // enc["group"]
                     d = float(enc["scales"][i, g]) * (q - float(enc["zeros"][i, g]))
+                elif enc["fmt"] == "bpdq":
+                    c = [float(v) for v in enc["coefs"][i, j // enc["group"]]]
+                    d = c[0]
+                    for t in range(b):  # plane t+1 is bit t of the code
+                        if (q >> t) & 1:
+                            d += c[t + 1]
                 else:
                     d = float(enc["lut"][i, q])
                 acc += d * x[j]
@@ -180,7 +186,8 @@ def _tiny_enc(bits, fmt, n_out, seed, M=6, K=64, B=2):
     idx = rng.choice(M * K, size=n_out, replace=False)
     W.ravel()[idx] = rng.uniform(0.3, 2.0, size=n_out) * np.where(rng.integers(0, 2, n_out) > 0, 1, -1)
     x = rng.standard_normal((B, K)).astype(np.float16)
-    enc = encode.encode(W, bits, fmt, n_out, 16, sens=x[0].astype(np.float64) ** 2)
+    group = 32 if fmt == "bpdq" else 16
+    enc = encode.encode(W, bits, fmt, n_out, group, sens=x[0].astype(np.float64) ** 2)
     return W, x, enc
 
 
@@ -190,7 +197,7 @@ def check_brute_force(enc, x):
     return bool(np.all(np.abs(y - yb) <= 1e-12 * (A + 1.0)))
 
 
-@pytest.mark.parametrize("bits,fmt", [(3, "uniform"), (4, "uniform"), (3, "lut"), (4, "lut")])
+@pytest.mark.parametrize("bits,fmt", [(3, "uniform"), (4, "uniform"), (3, "lut"), (4, "lut"), (3, "bpdq")])
 @pytest.mark.parametrize("n_out", [0, 5])
 def test_gemv_matches_brute_force(bits, fmt, n_out):
     W, x, enc = _tiny_enc(bits, fmt, n_out, seed=bits * 10 + n_out)
@@ -225,6 +232,20 @@ def test_brute_force_catches_transposed_lut(monkeypatch):
         e2["lut"] = e["lut"][:, ::-1].copy()
         return orig(e2, rows, codes)
     monkeypatch.setattr(gemv, "decode_rows", reversed_lut)
+    assert not check_brute_force(enc, x)
+
+
+def test_brute_force_catches_reversed_bit_planes(monkeypatch):
+    W, x, enc = _tiny_enc(3, "bpdq", 5, seed=10)
+    orig = gemv.decode_rows
+
+    def reversed_planes(e, rows=None, codes=None):
+        e2 = dict(e)
+        c = e["coefs"].copy()
+        c[:, :, 1:] = c[:, :, :0:-1]
+        e2["coefs"] = c
+        return orig(e2, rows, codes)
+    monkeypatch.setattr(gemv, "decode_rows", reversed_planes)
     assert not check_brute_force(enc, x)
 
 
@@ -669,3 +690,80 @@ def test_ssqr_encoding_is_exact_at_outliers():
     enc = encode.encode(W16, 3, "uniform", 10, pick="ssqr")
     assert 0 < int(enc["row_ptr"][-1]) <= 10
     check_exact_outliers(W16, enc)
+
+
+
+# ---------------------------------------------------------------------------
+# BPDQ ([BPDQ] "1. Formulation de la Grille Variable", "2. Cadre d'Optimisation")
+# ---------------------------------------------------------------------------
+def test_bpdq_fit_one_plane_is_class_means():
+    """With one plane the least-squares levels are the two class means:
+    C0 = mean(w | b = 0), C1 = mean(w | b = 1) - C0."""
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal(40)
+    q = rng.integers(0, 2, size=40)
+    c = encode.bpdq_fit(w, q, 1)
+    m0, m1 = w[q == 0].mean(), w[q == 1].mean()
+    assert np.allclose(c, [m0, m1 - m0], rtol=0, atol=1e-12)
+
+
+def test_bpdq_fit_catches_missing_intercept(monkeypatch):
+    def no_intercept(w, q, k):
+        A = np.stack([((q >> (i - 1)) & 1).astype(np.float64) for i in range(1, k + 1)], axis=1)
+        return np.concatenate([[0.0], np.linalg.lstsq(A, w, rcond=None)[0]])
+    monkeypatch.setattr(encode, "bpdq_fit", no_intercept)
+    with pytest.raises(AssertionError):
+        test_bpdq_fit_one_plane_is_class_means()
+
+
+def check_bpdq_assign_is_enumeration(assign):
+    """Each weight takes the bit pattern whose level C0 + sum_i C_i b_i is nearest,
+    found by listing all patterns (ties: lower code)."""
+    rng = np.random.default_rng(1)
+    k = 3
+    c = rng.standard_normal(k + 1) * 0.05
+    w = rng.standard_normal(200) * 0.1
+    q = assign(w, c, k)
+    for j in range(w.size):
+        best, bq = None, None
+        for code in range(1 << k):
+            lv = c[0] + sum(c[i] for i in range(1, k + 1) if (code >> (i - 1)) & 1)
+            e = abs(w[j] - lv)
+            if best is None or e < best:
+                best, bq = e, code
+        assert q[j] == bq, (j, q[j], bq)
+
+
+def test_bpdq_assign_is_enumeration():
+    check_bpdq_assign_is_enumeration(encode.bpdq_assign)
+
+
+def test_bpdq_assign_catches_msb_first_planes(monkeypatch):
+    def msb_levels(c, k):
+        q = np.arange(1 << k)
+        return c[0] + sum(c[i] * ((q >> (k - i)) & 1) for i in range(1, k + 1))
+    monkeypatch.setattr(encode, "bpdq_levels", msb_levels)
+    with pytest.raises(AssertionError):
+        check_bpdq_assign_is_enumeration(encode.bpdq_assign)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_bpdq_objective_never_increases(seed):
+    """Alternating exact bit updates and least-squares refits never raise the error."""
+    rng = np.random.default_rng(seed)
+    w = np.concatenate([rng.standard_normal(50) * 0.02, rng.standard_normal(14) * 0.08])
+    hist = []
+    encode.bpdq_group(w, 3, history=hist)
+    assert len(hist) >= 1
+    assert all(b <= a + 1e-15 for a, b in zip(hist, hist[1:]))
+
+
+def test_bpdq_contains_uniform_grids():
+    """The pages: the variable grid contains the uniform ones.  Weights on a
+    uniform 3-bit grid (C_i = 2^(i-1) s) are reproduced exactly."""
+    rng = np.random.default_rng(3)
+    s, lo = 2.0 ** -7, -2.0 ** -4
+    q = np.concatenate([np.arange(8), rng.integers(0, 8, size=56)])
+    w = (lo + s * q).astype(np.float16).astype(np.float64)
+    codes, c = encode.bpdq_group(w, 3)
+    assert np.array_equal(encode.bpdq_levels(c, 3)[codes], w)
