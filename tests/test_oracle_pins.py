@@ -767,3 +767,138 @@ def test_bpdq_contains_uniform_grids():
     w = (lo + s * q).astype(np.float16).astype(np.float64)
     codes, c = encode.bpdq_group(w, 3)
     assert np.array_equal(encode.bpdq_levels(c, 3)[codes], w)
+
+
+# ---------------------------------------------------------------------------
+# HPTQ: Huffman-coded integers on one unconstrained grid
+# ([Babai/GPTQ] "3. Applications Pratiques et Algorithmes")
+# ---------------------------------------------------------------------------
+from oracle import hptq  # noqa: E402
+
+
+def _huffman_cost(freq):
+    """Cost sum f_i l_i of an unlimited Huffman code, by repeatedly merging the two lightest."""
+    import heapq
+    h = [(float(f), i) for i, f in enumerate(freq)]
+    heapq.heapify(h)
+    cost, k = 0.0, len(freq)
+    while len(h) > 1:
+        a, _ = heapq.heappop(h)
+        b, _ = heapq.heappop(h)
+        cost += a + b
+        heapq.heappush(h, (a + b, k)); k += 1
+    return cost
+
+
+def _best_limited_cost(freq, L):
+    """Least sum f_i l_i over all length vectors with 1 <= l_i <= L and Kraft sum <= 1."""
+    import itertools
+    best = None
+    for ls in itertools.product(range(1, L + 1), repeat=len(freq)):
+        if sum(2.0 ** -l for l in ls) <= 1.0 + 1e-12:
+            c = sum(f * l for f, l in zip(freq, ls))
+            best = c if best is None or c < best else best
+    return best
+
+
+def check_package_merge(freq, L):
+    ln = hptq.package_merge_lengths(np.asarray(freq, dtype=np.float64), L)
+    assert ln.max() <= L
+    assert abs(sum(2.0 ** -int(l) for l in ln) - 1.0) < 1e-12, "not a complete prefix code"
+    assert sum(f * int(l) for f, l in zip(freq, ln)) == pytest.approx(_best_limited_cost(freq, L), abs=1e-9)
+
+
+@pytest.mark.parametrize("freq,L", [([5, 1, 1, 2, 9], 4), ([1, 1, 2, 3, 5, 8], 3), ([1, 1, 2, 3, 5, 8], 5),
+                                    ([4, 4, 4, 4], 2), ([7, 1], 1), ([3, 1, 1, 1, 1, 1], 3)])
+def test_package_merge_is_optimal_within_limit(freq, L):
+    check_package_merge(freq, L)
+
+
+def test_package_merge_catches_keeping_one_item_too_many(monkeypatch):
+    orig = hptq.package_merge_lengths
+
+    def plus_one(freq, max_len):
+        ln = orig(freq, max_len).copy()
+        ln[int(np.argmin(ln))] += 1
+        return ln
+    monkeypatch.setattr(hptq, "package_merge_lengths", plus_one)
+    with pytest.raises(AssertionError):
+        check_package_merge([5, 1, 1, 2, 9], 4)
+
+
+def test_package_merge_limit_binds_on_fibonacci_weights():
+    freq = [1, 1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144]  # an unlimited Huffman code reaches length 11
+    ln = hptq.package_merge_lengths(np.asarray(freq, float), 6)
+    assert ln.max() <= 6
+    assert abs(sum(2.0 ** -int(l) for l in ln) - 1.0) < 1e-12
+    cost = sum(f * int(l) for f, l in zip(freq, ln))
+    assert cost >= _huffman_cost(freq) - 1e-9
+    assert hptq.package_merge_lengths(np.asarray(freq, float), 16).max() == 11
+    assert sum(f * int(l) for f, l in zip(freq, hptq.package_merge_lengths(np.asarray(freq, float), 16))) \
+        == pytest.approx(_huffman_cost(freq))
+
+
+def check_canonical_prefix_free(sym, ln, codes):
+    words = [format(int(c), f"0{int(l)}b") for c, l in zip(codes, ln)]
+    for a in range(len(words)):
+        for b in range(len(words)):
+            if a != b:
+                assert not words[b].startswith(words[a]), (words[a], words[b])
+
+
+def test_canonical_code_is_prefix_free_and_round_trips():
+    rng = np.random.default_rng(0)
+    q = np.rint(rng.standard_normal((6, 256)) * 3).astype(np.int64)
+    q[2, 7] = 40  # a rare large integer
+    sym, ln, codes = hptq.build_code(q)
+    check_canonical_prefix_free(sym, ln, codes)
+    stream, row_bits = hptq.encode_stream(q, sym, ln, codes)
+    assert row_bits[-1] == sum(int(ln[list(sym).index(v)]) for v in q.ravel())
+    assert np.array_equal(hptq.decode_stream(stream, row_bits, 256, sym, ln, codes), q)
+
+
+def test_canonical_code_catches_wrong_increment(monkeypatch):
+    def bad(symbols, lengths):
+        order = np.lexsort((symbols, lengths))
+        s_, l_ = symbols[order], lengths[order]
+        c = np.zeros(len(s_), dtype=np.int64)
+        code, prev = 0, int(l_[0])
+        for k in range(1, len(s_)):
+            code = (code << (int(l_[k]) - prev)) + 1  # shift before the increment
+            prev = int(l_[k])
+            c[k] = code
+        return s_, l_, c
+    monkeypatch.setattr(hptq, "canonical_code", bad)
+    q = np.array([[0, 0, 0, 1, 1, 2, 3, -1, -1, -1, -1, 4]], dtype=np.int64)
+    with pytest.raises(AssertionError):
+        check_canonical_prefix_free(*hptq.build_code(q))
+
+
+def test_hptq_grid_has_no_clipping():
+    """Every weight, outliers included, sits within half a step of its grid point."""
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, planted = make_weights(wl, 0, 16, 512)
+    s, q = hptq.grid(W, 128, 0.8)
+    d = np.repeat(s, 128, axis=1) * q
+    w = W.astype(np.float64)
+    assert np.all(np.abs(w - d) <= 0.5 * np.repeat(s, 128, axis=1) * (1 + 1e-12))
+    assert np.abs(q[planted]).min() > np.abs(q[~planted]).max() // 4  # outliers take large integers
+
+
+def test_hptq_budget_boundary():
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, 8, 256)
+    a = hptq.budget_alpha(W, 128, 3.125)
+    bits = lambda t: hptq.stream_bits(hptq.grid(W, 128, t)[1])
+    assert bits(a) <= 3.125 * W.size
+    assert bits(a - 8.0 * 2.0 ** -40 * 4) > 3.125 * W.size
+
+
+def test_hptq_gemv_matches_plain_product_of_decoded_grid():
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, 8, 256)
+    enc = hptq.encode(W, 128, 3.125)
+    x = np.random.default_rng(1).standard_normal((2, 256)).astype(np.float16)
+    y, A = hptq.gemv(enc, x)
+    d = np.repeat(enc["scales"].astype(np.float64), 128, axis=1) * enc["q"]
+    assert np.allclose(y, x.astype(np.float64) @ d.T, rtol=0, atol=1e-12)
