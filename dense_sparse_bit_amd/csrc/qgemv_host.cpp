@@ -181,6 +181,13 @@ void unplace_chunk(int bits, int format, const uint32_t* w, uint32_t* c) {
 int qgemv_validate_shape(const qgemv_weights* w) {
   if (!w) return QGEMV_ERR_INVALID_ARG;
   if (w->M < 1 || w->K < 1 || w->nnz < 0) return QGEMV_ERR_INVALID_ARG;
+  if (w->format == QGEMV_FMT_HPTQ) {
+    if (w->group_size != kBlockK || w->K % kBlockK != 0 || w->K > kMaxK) return QGEMV_ERR_UNSUPPORTED;
+    if (w->nnz != 0) return QGEMV_ERR_UNSUPPORTED;  // one grid for inliers and outliers, no CSR
+    if (w->huff_nsym < 1 || w->huff_nsym > kHuffMaxSym) return QGEMV_ERR_UNSUPPORTED;
+    if ((int64_t)w->M * w->K > ((int64_t)1 << 40)) return QGEMV_ERR_UNSUPPORTED;
+    return QGEMV_OK;
+  }
   if (w->bits != 3 && w->bits != 4) return QGEMV_ERR_UNSUPPORTED;
   if (w->format != QGEMV_FMT_UNIFORM && w->format != QGEMV_FMT_LUT && w->format != QGEMV_FMT_BPDQ)
     return QGEMV_ERR_UNSUPPORTED;
@@ -199,9 +206,100 @@ int qgemv_validate_shape(const qgemv_weights* w) {
   return QGEMV_OK;
 }
 
+// HPTQ: the canonical codewords of the code (lengths non-decreasing, integers
+// ascending among equal lengths, Kraft sum <= 1), then every row decoded from
+// the stream; q gets the integers [M][K].  Returns a status.
+struct HuffCode {
+  std::vector<uint32_t> code;  // canonical codeword of each entry
+  int first[kHuffMaxLen + 1], count[kHuffMaxLen + 1], offset[kHuffMaxLen + 1];
+};
+
+static int hptq_code(const qgemv_weights* w, HuffCode& hc) {
+  const int n = w->huff_nsym;
+  if (!w->huff_len || !w->huff_sym) return QGEMV_ERR_INVALID_ARG;
+  double kraft = 0.0;
+  for (int l = 0; l <= kHuffMaxLen; ++l) hc.first[l] = hc.count[l] = hc.offset[l] = 0;
+  hc.code.assign(n, 0);
+  uint32_t code = 0;
+  for (int k = 0; k < n; ++k) {
+    const int l = w->huff_len[k], q = w->huff_sym[k];
+    if (l < 1 || l > kHuffMaxLen || q < -2048 || q > 2048) return QGEMV_ERR_INVALID_ARG;
+    if (k > 0) {
+      const int lp = w->huff_len[k - 1];
+      if (l < lp || (l == lp && q <= w->huff_sym[k - 1])) return QGEMV_ERR_INVALID_ARG;
+      code = (code + 1) << (l - lp);
+    }
+    hc.code[k] = code;
+    if (hc.count[l]++ == 0) {
+      hc.first[l] = (int)code;
+      hc.offset[l] = k;
+    }
+    kraft += std::ldexp(1.0, -l);
+  }
+  if (kraft > 1.0) return QGEMV_ERR_INVALID_ARG;
+  return QGEMV_OK;
+}
+
+static int hptq_decode(const qgemv_weights* w, const HuffCode& hc, std::vector<int16_t>& q) {
+  const int64_t M = w->M, K = w->K;
+  if (!w->codes || !w->row_bits || !w->scales) return QGEMV_ERR_INVALID_ARG;
+  if (w->row_bits[0] != 0) return QGEMV_ERR_INVALID_ARG;
+  q.assign((size_t)(M * K), 0);
+  for (int64_t i = 0; i < M; ++i) {
+    int64_t p = w->row_bits[i];
+    const int64_t end = w->row_bits[i + 1];
+    if (end < p) return QGEMV_ERR_INVALID_ARG;
+    for (int64_t j = 0; j < K; ++j) {
+      uint32_t c = 0;
+      int l = 0, sym = -1;
+      while (sym < 0) {
+        if (p >= end || l >= kHuffMaxLen) return QGEMV_ERR_INVALID_ARG;
+        c = (c << 1) | ((w->codes[p >> 3] >> (7 - (p & 7))) & 1u);
+        ++p;
+        ++l;
+        if (hc.count[l] && c >= (uint32_t)hc.first[l] && c - (uint32_t)hc.first[l] < (uint32_t)hc.count[l])
+          sym = hc.offset[l] + (int)(c - (uint32_t)hc.first[l]);
+      }
+      q[(size_t)(i * K + j)] = w->huff_sym[sym];
+    }
+    if (p != end) return QGEMV_ERR_INVALID_ARG;
+  }
+  const int64_t n = M * (K / kBlockK);
+  for (int64_t i = 0; i < n; ++i)
+    if (!half_finite(w->scales[i])) return QGEMV_ERR_INVALID_ARG;
+  return QGEMV_OK;
+}
+
+// Words of the HPTQ code section: every block's chunks, padded to 16 bytes.
+static uint64_t hptq_words(const qgemv_weights* w, const HuffCode& hc, const std::vector<int16_t>& q,
+                           std::vector<uint32_t>* hidx) {
+  const int M = w->M, K = w->K, nkb = K / kBlockK, tiles = (M + kTileRows - 1) / kTileRows;
+  std::vector<int> len_of(4097, 0);
+  for (int k = 0; k < w->huff_nsym; ++k) len_of[w->huff_sym[k] + 2048] = w->huff_len[k];
+  uint64_t words = 0;
+  if (hidx) hidx->assign((size_t)tiles * nkb + 1, 0);
+  for (int t = 0; t < tiles; ++t)
+    for (int b = 0; b < nkb; ++b) {
+      if (hidx) (*hidx)[(size_t)t * nkb + b] = (uint32_t)words;
+      uint64_t bits = 0;
+      for (int r = 0; r < kTileRows; ++r) {
+        const int row = t * kTileRows + r;
+        if (row >= M) continue;
+        for (int j = 0; j < kBlockK; ++j) bits += len_of[q[(size_t)row * K + b * kBlockK + j] + 2048];
+      }
+      words += ((bits + 31) / 32 + 3) / 4 * 4;
+    }
+  if (hidx) (*hidx)[(size_t)tiles * nkb] = (uint32_t)words;
+  return words;
+}
+
 static int validate_arrays(const qgemv_weights* w) {
   int st = qgemv_validate_shape(w);
   if (st) return st;
+  if (w->format == QGEMV_FMT_HPTQ) {
+    if (!w->row_ptr || w->row_ptr[0] != 0 || w->row_ptr[w->M] != 0) return QGEMV_ERR_MALFORMED_CSR;
+    return QGEMV_OK;  // the code and the stream are checked while they are decoded
+  }
   const int64_t M = w->M, K = w->K, nnz = w->nnz;
   if (!w->codes || !w->row_ptr) return QGEMV_ERR_INVALID_ARG;
   if (nnz > 0 && (!w->col_idx || !w->values)) return QGEMV_ERR_INVALID_ARG;
@@ -252,16 +350,110 @@ void qgemv_set_hip_error(int e) { g_last_hip_error = e; }
 
 extern "C" {
 
+// The blob header of a validated descriptor (HPTQ: decodes the stream to size the code section).
+static int header_of(const qgemv_weights* w, BlobHeader& h, HuffCode* hc_out = nullptr,
+                     std::vector<int16_t>* q_out = nullptr) {
+  int st = validate_arrays(w);
+  if (st) return st;
+  uint32_t words = 0;
+  if (w->format == QGEMV_FMT_HPTQ) {
+    HuffCode hc;
+    std::vector<int16_t> q;
+    if ((st = hptq_code(w, hc))) return st;
+    if ((st = hptq_decode(w, hc, q))) return st;
+    const uint64_t nw = hptq_words(w, hc, q, nullptr);
+    if (nw >= ((uint64_t)1 << 29)) return QGEMV_ERR_UNSUPPORTED;
+    words = (uint32_t)nw;
+    if (hc_out) *hc_out = hc;
+    if (q_out) q_out->swap(q);
+  }
+  h = make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz, w->huff_nsym, words);
+  if (h.total_bytes >= ((uint64_t)1 << 31)) return QGEMV_ERR_UNSUPPORTED;
+  return QGEMV_OK;
+}
+
 int qgemv_packed_size(const qgemv_weights* w, size_t* bytes) {
   if (!bytes) return QGEMV_ERR_INVALID_ARG;
-  const int st = validate_arrays(w);
+  BlobHeader h;
+  const int st = header_of(w, h);
   if (st) return st;
-  *bytes = (size_t)make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz).total_bytes;
+  *bytes = (size_t)h.total_bytes;
+  return QGEMV_OK;
+}
+
+// HPTQ repack: every block's chunks re-laid from the stream, the steps, the
+// block and lane offsets and the decode tables (see qgemv_layout.h).
+static void put_bits(uint32_t* words, uint64_t pos, uint32_t code, int len) {
+  for (int i = 0; i < len; ++i) {
+    const uint64_t p = pos + (uint64_t)i;
+    words[p >> 5] |= ((code >> (len - 1 - i)) & 1u) << (31 - (p & 31));
+  }
+}
+
+static int repack_hptq(const qgemv_weights* w, void* dst_host, size_t bytes) {
+  BlobHeader h;
+  HuffCode hc;
+  std::vector<int16_t> q;
+  const int st = header_of(w, h, &hc, &q);
+  if (st) return st;
+  if (bytes < h.total_bytes) return QGEMV_ERR_SIZE;
+  uint8_t* blob = (uint8_t*)dst_host;
+  std::memset(blob, 0, (size_t)h.total_bytes);
+  std::memcpy(blob, &h, sizeof(h));
+  const int M = w->M, K = w->K, nkb = h.nkb, tiles = h.tiles, n = w->huff_nsym;
+  std::vector<uint32_t> cw(4097, 0);
+  std::vector<int> cl(4097, 0);
+  for (int k = 0; k < n; ++k) {
+    cw[w->huff_sym[k] + 2048] = hc.code[k];
+    cl[w->huff_sym[k] + 2048] = w->huff_len[k];
+  }
+  std::vector<uint32_t> hidx;
+  hptq_words(w, hc, q, &hidx);
+  uint32_t* words = (uint32_t*)(blob + h.off_codes);
+  uint16_t* hlane = (uint16_t*)(blob + h.off_hlane);
+  uint16_t* steps = (uint16_t*)(blob + h.off_meta);
+  for (int t = 0; t < tiles; ++t)
+    for (int b = 0; b < nkb; ++b) {
+      const size_t blk = (size_t)t * nkb + b;
+      const uint64_t base = (uint64_t)hidx[blk] * 32;
+      uint32_t p = 0;
+      for (int l = 0; l < 64; ++l) {
+        hlane[blk * 64 + l] = (uint16_t)p;
+        const int row = t * kTileRows + l % 16;
+        if (row >= M) continue;
+        for (int j = 0; j < kChunkCodes; ++j) {
+          const int v = q[(size_t)row * K + b * kBlockK + 32 * (l / 16) + j] + 2048;
+          put_bits(words, base + p, cw[v], cl[v]);
+          p += (uint32_t)cl[v];
+        }
+      }
+      for (int r = 0; r < kTileRows; ++r) {
+        const int row = t * kTileRows + r;
+        steps[blk * kTileRows + r] = row < M ? w->scales[(size_t)row * nkb + b] : 0;
+      }
+    }
+  std::memcpy(blob + h.off_hidx, hidx.data(), 4 * hidx.size());
+  int32_t* tab = (int32_t*)(blob + h.off_htab);
+  for (int k = 0; k < n; ++k) {
+    const int l = w->huff_len[k];
+    if (l > kHuffBits) continue;
+    const int32_t e = (int32_t)((uint32_t)(int32_t)w->huff_sym[k] << 8) | l;
+    const uint32_t lo = hc.code[k] << (kHuffBits - l);
+    for (uint32_t s = 0; s < (1u << (kHuffBits - l)); ++s) tab[lo + s] = e;
+  }
+  int32_t* slow = tab + kHuffTable;
+  for (int l = 0; l <= kHuffMaxLen; ++l) {
+    slow[l] = hc.first[l];
+    slow[17 + l] = hc.count[l];
+    slow[34 + l] = hc.offset[l];
+  }
+  std::memcpy(blob + h.off_hsym, w->huff_sym, 2 * (size_t)n);
   return QGEMV_OK;
 }
 
 int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
   if (!dst_host) return QGEMV_ERR_INVALID_ARG;
+  if (w && w->format == QGEMV_FMT_HPTQ) return repack_hptq(w, dst_host, bytes);
   const int st = validate_arrays(w);
   if (st) return st;
   const BlobHeader h = make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz);
@@ -367,6 +559,7 @@ int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out) {
   std::memcpy(&h, blob_host, sizeof(h));
   if (h.magic != kMagic || h.version != kVersion) return QGEMV_ERR_SIZE;
   if (h.total_bytes > bytes) return QGEMV_ERR_SIZE;
+  if (h.format == QGEMV_FMT_HPTQ) return QGEMV_ERR_UNSUPPORTED;
   const uint8_t* blob = (const uint8_t*)blob_host;
   const int chunk_bytes = 4 * h.bits;
   uint32_t c[32], dw[4] = {0, 0, 0, 0};

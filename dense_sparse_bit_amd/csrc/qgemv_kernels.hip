@@ -1241,6 +1241,163 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// HPTQ, batch 1: prefix-coded integers on one grid.
+//
+// A (tile, K-block) block holds its 64 lanes' 32-codeword chunks as one bit
+// sequence (qgemv_layout.h).  A wave copies a block's words into its own LDS
+// buffer; each lane keeps the next bits of its chunk in a 64-bit register
+// buffer, refilled from LDS every two codewords (a codeword has at most 16
+// bits), and looks the top 10 bits up in a 1024-entry table in LDS that
+// gives the integer and length of the codeword they start with; a longer
+// codeword is found from the canonical first codeword of each length.  The
+// integers are exact in FP16 and form the A operand of four MFMAs against x;
+// each row's step scales the block's sums in fp32.  The blocks of a
+// workgroup are cut into 16 runs, one per wave, with a partial slot per
+// (wave, tile) as in k_xlds, and the outputs add the slots in wave order.
+// The next block's first 1 KiB of code words, lane offset and steps are
+// loaded while the current block is decoded.
+// ---------------------------------------------------------------------------
+constexpr int kHuffBufWords = 1024 + 8;  // a block's largest code (64 * 32 * 16 bits) and a spill
+
+__global__ void __launch_bounds__(64 * kWaves)
+k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, const uint32_t* __restrict__ hidx,
+       const uint16_t* __restrict__ hlane, const int32_t* __restrict__ htab, const int16_t* __restrict__ hsym,
+       const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K, int nkb, int tiles, int nsym,
+       uint32_t nwords) {
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T0 = (int)((int64_t)blockIdx.x * tiles / gridDim.x);
+  const int T1 = (int)((int64_t)(blockIdx.x + 1) * tiles / gridDim.x);
+  const int TW = T1 - T0;
+  const int nrows = min(TW * 16, M - T0 * 16);
+  const int L = TW * nkb;
+  const int b0 = w * L / kWaves, b1 = (w + 1) * L / kWaves;  // this wave's run
+
+  // LDS: xs [K] FP16 | table [1024] | first, count, offset [3][17] (+1) | integers [nsym] int16 (padded)
+  //      | slots [TW+15][16] | code buffers [16][kHuffBufWords]
+  uint16_t* xs = (uint16_t*)lds;
+  int32_t* tab = (int32_t*)(lds + K / 2);
+  int32_t* slow = tab + kHuffTable;
+  int16_t* syms = (int16_t*)(slow + 52);
+  float* slots = (float*)(slow + 52 + ((nsym + 1) / 2 + 3) / 4 * 4);
+  uint32_t* buf = (uint32_t*)(slots + (TW + 15) * 16) + w * kHuffBufWords;
+
+  for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
+  for (int i = threadIdx.x; i < kHuffTable + 51; i += 64 * kWaves) tab[i] = htab[i];
+  for (int i = threadIdx.x; i < nsym; i += 64 * kWaves) syms[i] = hsym[i];
+
+  const rsrc_t rw = make_rsrc(words, nwords * 4u);
+  u32x4_t pre = {0u, 0u, 0u, 0u};
+  uint32_t lbn = 0, stn0 = 0, stn1 = 0;
+  auto prefetch = [&](int bb) {  // first 1 KiB of block bb's words, lane offset, steps of rows 4*(lane/16) .. +3
+    if (bb < b1) {
+      const int g = T0 * nkb + bb;
+      const uint32_t wo = hidx[g];
+      pre = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + 4u * (uint32_t)lane) * 4u), 0, kNonTemporal);
+      lbn = hlane[(size_t)g * 64 + lane];
+      const uint32_t* sp = (const uint32_t*)(steps + (size_t)g * 16 + 4 * (lane >> 4));
+      stn0 = sp[0];
+      stn1 = sp[1];
+    }
+  };
+  prefetch(b0);
+  __syncthreads();
+
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int tl = b0 / nkb;
+  auto flush = [&]() {  // acc[i]: row 4*(lane/16) + i of local tile tl
+    if ((lane & 15) == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) slots[(w + tl) * 16 + 4 * (lane >> 4) + i] = acc[i];
+  };
+  const int sl = 32 * (lane >> 4);
+  for (int bb = b0; bb < b1; ++bb) {
+    const int t = bb / nkb, kb = bb - t * nkb;
+    if (t != tl) {
+      flush();
+      acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      tl = t;
+    }
+    const int g = T0 * nkb + bb;
+    const uint32_t wo = hidx[g], nw = hidx[g + 1] - wo;  // a multiple of 4
+    // the block's words into this wave's buffer: the first 1 KiB from the prefetch, any more now
+    if (4 * lane < (int)nw) ((u32x4_t*)buf)[lane] = pre;
+    for (uint32_t i = 256u + 4u * (uint32_t)lane; i < nw; i += 256u)
+      *(u32x4_t*)(buf + i) = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + i) * 4u), 0, kNonTemporal);
+    if (lane < 2) buf[nw + lane] = 0u;
+    const uint32_t lb = lbn, st0 = stn0, st1 = stn1;
+    prefetch(bb + 1);
+
+    // decode this lane's 32 codewords
+    uint32_t qh[16];
+    const bool real = T0 * 16 + t * 16 + (lane & 15) < M;
+    if (real) {
+      uint32_t wi = (lb >> 5) + 2;
+      const uint32_t s0 = lb & 31u;
+      uint64_t bits = (((uint64_t)buf[lb >> 5] << 32) | buf[(lb >> 5) + 1]) << s0;
+      int nb = 64 - (int)s0;
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) {
+        const uint32_t nxt = buf[wi];
+        if (nb < 32) {  // two codewords always fit after a refill
+          bits |= (uint64_t)nxt << (32 - nb);
+          nb += 32;
+          ++wi;
+        }
+        int32_t q2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t win = (uint32_t)(bits >> 32);
+          const int32_t e = tab[win >> (32 - kHuffBits)];
+          int len = e & 255;
+          int32_t q = e >> 8;
+          if (len == 0) {  // a codeword longer than the table's index
+            for (int l = kHuffBits + 1; l <= kHuffMaxLen; ++l) {
+              const uint32_t c = win >> (32 - l);
+              if (c - (uint32_t)slow[l] < (uint32_t)slow[17 + l]) {
+                q = syms[slow[34 + l] + (int)(c - (uint32_t)slow[l])];
+                len = l;
+                break;
+              }
+            }
+          }
+          bits <<= len;
+          nb -= len;
+          q2[u] = q;
+        }
+        const _Float16 h0 = (_Float16)(float)q2[0], h1 = (_Float16)(float)q2[1];
+        qh[j / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qh[j] = 0u;
+    }
+    floatx4_t blk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half8_t bx = *(const half8_t*)(xs + kb * kBlockK + sl + 8 * i);
+      blk = mfma(h8(qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]), bx, blk);
+    }
+    acc[0] += (float)__builtin_bit_cast(_Float16, (uint16_t)st0) * blk[0];
+    acc[1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(st0 >> 16)) * blk[1];
+    acc[2] += (float)__builtin_bit_cast(_Float16, (uint16_t)st1) * blk[2];
+    acc[3] += (float)__builtin_bit_cast(_Float16, (uint16_t)(st1 >> 16)) * blk[3];
+  }
+  if (b0 < b1) flush();
+  __syncthreads();
+  for (int r = threadIdx.x; r < nrows; r += 64 * kWaves) {
+    const int t = r >> 4;
+    float v = 0.f;
+    for (int u = 0; u < kWaves; ++u) {
+      const int c0 = u * L / kWaves, c1 = (u + 1) * L / kWaves;
+      if (c0 < c1 && c0 / nkb <= t && t <= (c1 - 1) / nkb) v += slots[(u + t) * 16 + (r & 15)];
+    }
+    y[T0 * 16 + r] = v;
+  }
+}
+
 // Debug: decode the blob's codes back to canonical order, one thread per 32-code chunk.
 template <int FMT, int BITS>
 __global__ void __launch_bounds__(256)
@@ -1473,6 +1630,25 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   return hipGetLastError();
 }
 
+// HPTQ, batch 1: one workgroup per CU over its tile range.
+hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+  const BlobHeader& h = p->h;
+  const int grid = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
+  const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
+  size_t lds = (size_t)h.K * 2 + (size_t)(kHuffTable + 52) * 4 + (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4 +
+               (tw + 15) * 16 * 4 + (size_t)kWaves * kHuffBufWords * 4;
+  if (lds > kLdsBytes) return hipErrorInvalidValue;
+  if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_huff, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(k_huff, dim3(grid), dim3(64 * kWaves), lds, st, (const uint32_t*)(p->blob + h.off_codes),
+                     (const uint16_t*)(p->blob + h.off_meta), (const uint32_t*)(p->blob + h.off_hidx),
+                     (const uint16_t*)(p->blob + h.off_hlane), (const int32_t*)(p->blob + h.off_htab),
+                     (const int16_t*)(p->blob + h.off_hsym), x, y, h.M, h.K, h.nkb, h.tiles, h.hsym, h.hwords);
+  return hipGetLastError();
+}
+
 template <int FMT, int BITS>
 hipError_t launch_run(const qgemv_plan* p, const uint16_t* x, float* y, int batch, hipStream_t st) {
   if (batch == 1) {
@@ -1510,12 +1686,18 @@ int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* pack
   const int st = qgemv_validate_shape(shape);
   if (st) return st;
   if ((uintptr_t)packed_dev % kAlign) return QGEMV_ERR_INVALID_ARG;
-  const BlobHeader expect =
-      make_header(shape->M, shape->K, shape->bits, shape->format, shape->group_size, shape->nnz);
+  const bool hptq = shape->format == QGEMV_FMT_HPTQ;
+  BlobHeader expect =
+      make_header(shape->M, shape->K, shape->bits, shape->format, shape->group_size, shape->nnz, shape->huff_nsym, 0);
   if (bytes < expect.total_bytes) return QGEMV_ERR_SIZE;
   BlobHeader got;
   const hipError_t e = hipMemcpy(&got, packed_dev, sizeof(got), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_status(e);
+  if (hptq) {  // the code section's size comes from the stream, so from the blob
+    expect = make_header(shape->M, shape->K, shape->bits, shape->format, shape->group_size, shape->nnz,
+                         shape->huff_nsym, got.hwords);
+    if (bytes < expect.total_bytes) return QGEMV_ERR_SIZE;
+  }
   if (std::memcmp(&got, &expect, sizeof(got)) != 0) return QGEMV_ERR_SIZE;
   qgemv_plan* p = new (std::nothrow) qgemv_plan{expect, (const uint8_t*)packed_dev};
   if (!p) return QGEMV_ERR_INVALID_ARG;
@@ -1531,6 +1713,10 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
   const uint16_t* x = (const uint16_t*)x_dev;
   const bool b4 = h->h.bits == 4;
   hipError_t e;
+  if (h->h.format == QGEMV_FMT_HPTQ) {
+    if (batch != 1) return QGEMV_ERR_UNSUPPORTED;
+    return hip_status(launch_huff(h, x, y_dev, st));
+  }
   if (h->h.format == QGEMV_FMT_LUT)
     e = b4 ? launch_run<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_run<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
   else if (h->h.format == QGEMV_FMT_BPDQ)
@@ -1543,6 +1729,7 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
 
 int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream) {
   if (!h || !codes_dev) return QGEMV_ERR_INVALID_ARG;
+  if (h->h.format == QGEMV_FMT_HPTQ) return QGEMV_ERR_UNSUPPORTED;
   if ((uintptr_t)codes_dev % 16) return QGEMV_ERR_INVALID_ARG;
   const hipStream_t st = (hipStream_t)stream;
   hipError_t e;

@@ -38,10 +38,25 @@
 //
 //   BPDQ codes (3 bit) use the L3 placement.
 //
+//   HPTQ codes (prefix codewords, 32 per lane chunk): for each (tile,
+//   K-block) the 64 chunks' codewords in lane order, as one bit sequence
+//   stored in 32-bit words most significant bit first (bit p is bit 31 -
+//   p % 32 of word p / 32), starting on a 16-byte boundary; hidx holds each
+//   block's first word (and the end), hlane each lane's bit offset inside its
+//   block.  Chunks of padding rows are empty.
+//
 // meta    LUT: per row (tiles*16 rows) the canonical FP16 table, 2^bits entries.
 //         BPDQ: per (tile, K-block) the FP16 coefficients [16 rows][128/group
 //         groups][bits + 1] (C0 first); a lane's chunk lies in one group, whose
 //         coefficients are one 8-byte piece.
+//         HPTQ: per (tile, K-block) the 16 rows' FP16 steps (group 128 = the
+//         K-block).
+// hidx    HPTQ: uint32 [tiles*nkb + 1]; hlane: uint16 [tiles*nkb*64];
+// htab    HPTQ: int32 [1024]: for the next 10 bits of a chunk, (q << 8) | len
+//         of the codeword they start with if len <= 10, else 0; then int32
+//         [3][17]: per length l the first canonical codeword, the number of
+//         codewords and the index of the first in hsym.
+// hsym    HPTQ: int16 [hsym]: the codewords' integers in canonical order.
 //         UNIFORM: 512 bytes per (tile, K-block) for its 16 rows x 8 groups of
 //         16 codes: a z plane, FP16 zero points [row][group] (256 B), then an
 //         s plane, FP16 scales [group / 2][row][group % 2] (256 B).  Lane l's
@@ -63,13 +78,17 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 4;
+constexpr uint32_t kVersion = 5;
 constexpr int kTileRows = 16;
 constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
 constexpr int kMaxK = 16384;
 constexpr uint64_t kAlign = 256;
 constexpr uint64_t kHeaderBytes = 256;
+constexpr int kHuffBits = 10;               // HPTQ decode table index: the next 10 bits
+constexpr int kHuffTable = 1 << kHuffBits;
+constexpr int kHuffMaxLen = 16;
+constexpr int kHuffMaxSym = 4096;
 
 struct BlobHeader {
   uint32_t magic;
@@ -82,6 +101,11 @@ struct BlobHeader {
   int32_t Kp;                // K padded to a multiple of kBlockK
   int32_t nkb;               // Kp / kBlockK
   uint64_t off_boff, off_bent;  // outliers grouped by (tile, K-block)
+  // HPTQ only (0 otherwise): block word offsets, lane bit offsets, decode
+  // tables, codeword integers; number of codewords and of code words.
+  uint64_t off_hidx, off_hlane, off_htab, off_hsym;
+  int32_t hsym;
+  uint32_t hwords;
 };
 static_assert(sizeof(BlobHeader) <= kHeaderBytes, "header too large");
 
@@ -89,7 +113,9 @@ inline uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign
 
 // Section offsets of a blob for the given shape.
 inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format, int32_t group,
-                              int64_t nnz) {
+                              int64_t nnz, int32_t hsym = 0, uint32_t hwords = 0) {
+  const bool hptq = format == 3;
+  if (hptq) bits = 0;
   BlobHeader h{};
   h.magic = kMagic;
   h.version = kVersion;
@@ -105,17 +131,27 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
   h.block_bytes = (uint32_t)(64 * 4 * bits);
   h.meta_unit_bytes = format == 0   ? 64u * 8u
                       : format == 1 ? (uint32_t)(2u << bits)
+                      : hptq        ? (uint32_t)(kTileRows * 2)
                                     : (uint32_t)(kTileRows * (kBlockK / (group > 0 ? group : kBlockK)) * (bits + 1) * 2);
   const uint64_t nblocks = (uint64_t)h.tiles * h.nkb;
   const uint64_t meta_bytes =
       format == 1 ? (uint64_t)h.tiles * kTileRows * h.meta_unit_bytes : nblocks * h.meta_unit_bytes;
   h.off_codes = kHeaderBytes;
-  h.off_meta = align_up(h.off_codes + nblocks * h.block_bytes);
+  h.hsym = hptq ? hsym : 0;
+  h.hwords = hptq ? hwords : 0;
+  h.off_meta = align_up(h.off_codes + (hptq ? 4ull * hwords : nblocks * h.block_bytes));
   h.off_rowptr = align_up(h.off_meta + meta_bytes);
   h.off_entries = align_up(h.off_rowptr + 4ull * ((uint64_t)M + 1));
   h.off_boff = align_up(h.off_entries + 4ull * (uint64_t)nnz);
   h.off_bent = align_up(h.off_boff + 4ull * (nblocks + 1));
   h.total_bytes = align_up(h.off_bent + 4ull * (uint64_t)nnz);
+  if (hptq) {
+    h.off_hidx = h.total_bytes;
+    h.off_hlane = align_up(h.off_hidx + 4ull * (nblocks + 1));
+    h.off_htab = align_up(h.off_hlane + 2ull * 64ull * nblocks);
+    h.off_hsym = align_up(h.off_htab + 4ull * (kHuffTable + 3 * 17));
+    h.total_bytes = align_up(h.off_hsym + 2ull * (uint64_t)hsym);
+  }
   return h;
 }
 

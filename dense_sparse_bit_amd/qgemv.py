@@ -9,7 +9,9 @@ Canonical arrays are passed as a dict with the keys of the C struct
 ``qgemv_weights``: M, K, bits, fmt ("uniform" | "lut" | "bpdq"), group,
 codes_packed (uint8 [M, K*bits/8]), scales / zeros (FP16 [M, K/16]), lut (FP16
 [M, 2^bits]) or coefs (FP16 [M, K/group, bits+1]), row_ptr (int32 [M+1]),
-col_idx (int32 [nnz]), values (FP16 [nnz]).
+col_idx (int32 [nnz]), values (FP16 [nnz]); "hptq" instead: stream (bytes),
+row_bits (int64 [M+1]), huff_len (uint8), huff_sym (int16), scales (FP16
+[M, K/128]).
 """
 
 from __future__ import annotations
@@ -24,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsb_qgemv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qgemv.h")
 
-FMT = {"uniform": 0, "lut": 1, "bpdq": 2}
+FMT = {"uniform": 0, "lut": 1, "bpdq": 2, "hptq": 3}
 STATUS = {0: "QGEMV_OK", -1: "QGEMV_ERR_INVALID_ARG", -2: "QGEMV_ERR_MALFORMED_CSR",
           -3: "QGEMV_ERR_UNSUPPORTED", -4: "QGEMV_ERR_HIP", -5: "QGEMV_ERR_SIZE"}
 
@@ -42,6 +44,8 @@ class Weights(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
         ("lut", ctypes.c_void_p), ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
         ("values", ctypes.c_void_p), ("coefs", ctypes.c_void_p),
+        ("huff_nsym", ctypes.c_int32), ("huff_len", ctypes.c_void_p), ("huff_sym", ctypes.c_void_p),
+        ("row_bits", ctypes.c_void_p),
     ]
 
 
@@ -104,10 +108,10 @@ def make_weights(w: dict):
     row_ptr = np.asarray(w["row_ptr"])
     nnz = int(row_ptr[-1]) if len(row_ptr) else 0
     s = Weights()
-    s.M, s.K, s.bits, s.format = int(w["M"]), int(w["K"]), int(w["bits"]), fmt
+    s.M, s.K, s.bits, s.format = int(w["M"]), int(w["K"]), int(w.get("bits", 0)), fmt
     s.group_size = int(w.get("group", 16) or 16)
     s.nnz = int(w.get("nnz", nnz))
-    s.codes = ptr(w["codes_packed"], np.uint8)
+    s.codes = ptr(w["codes_packed"] if "codes_packed" in w else w["stream"], np.uint8)
     s.scales = ptr(w.get("scales"), np.uint16)
     s.zeros = ptr(w.get("zeros"), np.uint16)
     s.lut = ptr(w.get("lut"), np.uint16)
@@ -115,6 +119,12 @@ def make_weights(w: dict):
     s.col_idx = ptr(w.get("col_idx"), np.int32) if nnz else None
     s.values = ptr(w.get("values"), np.uint16) if nnz else None
     s.coefs = ptr(w.get("coefs"), np.uint16)
+    if w.get("huff_sym") is not None:  # HPTQ: the prefix code and the row starts in the stream
+        s.huff_nsym = len(w["huff_sym"])
+        s.huff_len = ptr(w["huff_len"], np.uint8)
+        s.huff_sym = ptr(w["huff_sym"], np.int16)
+        s.row_bits = ptr(w["row_bits"], np.int64)
+        s.bits = 0
     return s, keep
 
 

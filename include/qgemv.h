@@ -18,6 +18,12 @@
  * Models", section "1. Formulation de la Grille Variable": the code's bit
  * planes select per-group FP16 coefficients, d = C0 + sum_t C_t * B_t.
  *
+ * A fourth, QGEMV_FMT_HPTQ, follows the page on GPTQ as Babai's algorithm,
+ * section "3. Applications Pratiques et Algorithmes" (HPTQ): every weight,
+ * outliers included, is an integer on one unclipped grid with an FP16 step
+ * per row and group of 128, and the integers are stored as a canonical
+ * prefix (Huffman) code; there is no sparse part.
+ *
  * Flow: qgemv_packed_size + qgemv_repack (host, offline) turn the canonical
  * arrays below into one self-describing blob laid out for the gfx950 kernels;
  * the caller copies the blob to device memory it owns; qgemv_create binds a
@@ -54,8 +60,10 @@ typedef enum {
 typedef enum {
   QGEMV_FMT_UNIFORM = 0, /* d = scale[i][g] * (q - zero[i][g]),  g = j / group_size */
   QGEMV_FMT_LUT = 1,     /* d = lut[i][q]                                            */
-  QGEMV_FMT_BPDQ = 2     /* d = coefs[i][g][0] + sum_{t=1..bits} coefs[i][g][t] *
+  QGEMV_FMT_BPDQ = 2,    /* d = coefs[i][g][0] + sum_{t=1..bits} coefs[i][g][t] *
                             ((q >> (t-1)) & 1),  g = j / group_size                  */
+  QGEMV_FMT_HPTQ = 3     /* d = scale[i][g] * q, q the integer of weight (i, j)'s
+                            prefix codeword in the stream,  g = j / 128             */
 } qgemv_format;
 
 /*
@@ -78,6 +86,24 @@ typedef enum {
  *   coefs       FP16 bits [M][K/group_size][bits+1] (BPDQ), else NULL: the
  *               group's C0, then C1 .. C_bits (plane t = bit t-1 of the code).
  *               Finite.
+ *
+ * QGEMV_FMT_HPTQ uses these instead of the fixed-width fields:
+ *   bits        ignored; group_size 128; K % 128 == 0; nnz 0 (no CSR).
+ *   codes       the stream: one sequence of codewords, row 0 first, each
+ *               written most significant bit first, packed into bytes most
+ *               significant bit first; row i starts at bit row_bits[i].
+ *   scales      FP16 bits [M][K/128], finite: the steps.
+ *   huff_nsym   number of codewords, 1 .. 4096.
+ *   huff_len    uint8 [huff_nsym]: codeword lengths 1 .. 16, non-decreasing,
+ *               with sum 2^-len <= 1.
+ *   huff_sym    int16 [huff_nsym]: the integer of each codeword, |q| <= 2048,
+ *               strictly ascending among codewords of equal length.  The
+ *               codewords are canonical: in this order, each is the previous
+ *               one plus 1, shifted left by the growth in length (the first
+ *               is all zeros).
+ *   row_bits    int64 [M+1]: row_bits[0] = 0, row i holds exactly K codewords
+ *               in bits [row_bits[i], row_bits[i+1]).
+ * An HPTQ plan runs at batch 1 only (UNSUPPORTED otherwise).
  *   row_ptr     int32 [M+1]: row_ptr[0] = 0, non-decreasing, row_ptr[M] = nnz.
  *   col_idx     int32 [nnz]: 0 <= c < K, strictly ascending inside a row.
  *   values      FP16 bits [nnz], finite.  col_idx/values may be NULL iff nnz == 0.
@@ -96,6 +122,10 @@ typedef struct {
   const int32_t* col_idx;
   const uint16_t* values;
   const uint16_t* coefs;
+  int32_t huff_nsym;
+  const uint8_t* huff_len;
+  const int16_t* huff_sym;
+  const int64_t* row_bits;
 } qgemv_weights;
 
 typedef struct qgemv_plan* qgemv_handle;
@@ -118,9 +148,10 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes);
 /*
  * Host-side inverse of the code repacking: read a blob in host memory and
  * write the canonical codes, one uint8 per weight, to codes_out [M][K] (host).
- * For tests of the repacker without a GPU.
+ * For tests of the repacker without a GPU.  HPTQ blobs: UNSUPPORTED (their
+ * integers do not fit one byte).
  * Errors: INVALID_ARG (null pointer), SIZE (blob shorter than its header says
- * or header not recognised).
+ * or header not recognised), UNSUPPORTED.
  */
 int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out);
 
@@ -152,7 +183,7 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
  * Enqueue a kernel that decodes the blob's codes back to canonical order, one
  * uint8 per weight, into codes_dev [M][K] (device memory).  Uses the same
  * unpacking as the product kernels; for bit-exact checks of the codes.
- * Errors: INVALID_ARG, HIP.
+ * Errors: INVALID_ARG, HIP, UNSUPPORTED (HPTQ plans).
  */
 int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream);
 

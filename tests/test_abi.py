@@ -246,3 +246,88 @@ def test_bpdq_validation():
     c = base["coefs"].copy(); c[0, 0] = [40000.0, 30000.0, 0.0, 0.0]  # a level beyond FP16 range
     w = dict(base); w["coefs"] = c
     assert _status(w) == UNS
+
+
+# ---------------------------------------------------------------------------
+# HPTQ blobs
+# ---------------------------------------------------------------------------
+def _hptq_enc(M=21, K=512, seed=0):
+    from oracle import hptq
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, M, K)
+    return hptq.encode(W, 128, 3.125 + 0.25 * seed)
+
+
+def _decode_hptq_blob(blob):
+    """The blob's integers [M, K] and steps, read the way the table decoder reads them."""
+    hdr32 = blob[:256].view(np.int32)
+    off = blob[:256].view(np.uint64)
+    M, K, tiles = int(hdr32[2]), int(hdr32[3]), int(hdr32[7])
+    nkb = int(hdr32[23])
+    off_codes, off_meta, off_hidx, off_hlane, off_htab, off_hsym = (int(off[i]) for i in (5, 6, 14, 15, 16, 17))
+    nsym = int(hdr32[36])
+    hidx = blob[off_hidx:off_hidx + 4 * (tiles * nkb + 1)].view(np.uint32)
+    words = blob[off_codes:off_codes + 4 * int(hidx[-1]) + 8].view(np.uint32)
+    words = np.concatenate([words, np.zeros(2, np.uint32)])
+    hlane = blob[off_hlane:off_hlane + 2 * 64 * tiles * nkb].view(np.uint16)
+    tab = blob[off_htab:off_htab + 4 * (1024 + 51)].view(np.int32)
+    first, count, offs = tab[1024:1041], tab[1041:1058], tab[1058:1075]
+    syms = blob[off_hsym:off_hsym + 2 * nsym].view(np.int16)
+    q = np.zeros((tiles * 16, nkb * 128), dtype=np.int64)
+    for blk in range(tiles * nkb):
+        t, b = divmod(blk, nkb)
+        base = int(hidx[blk]) * 32
+        for l in range(64):
+            if t * 16 + l % 16 >= M:
+                continue
+            p = base + int(hlane[blk * 64 + l])
+            for j in range(32):
+                w0, w1 = int(words[p >> 5]), int(words[(p >> 5) + 1])
+                win = ((w0 << 32 | w1) >> (32 - (p & 31))) & 0xFFFFFFFF
+                e = int(tab[win >> 22])
+                if e & 255:
+                    ln, v = e & 255, e >> 8
+                else:
+                    for ln in range(11, 17):
+                        c = win >> (32 - ln)
+                        if count[ln] and first[ln] <= c < first[ln] + count[ln]:
+                            v = int(syms[offs[ln] + c - first[ln]])
+                            break
+                    else:
+                        raise AssertionError("no codeword")
+                q[t * 16 + l % 16, b * 128 + 32 * (l // 16) + j] = v
+                p += ln
+    steps = blob[off_meta:off_meta + 32 * tiles * nkb].view(np.uint16).reshape(tiles, nkb, 16)
+    steps = steps.transpose(0, 2, 1).reshape(tiles * 16, nkb)
+    return q[:M, :K], steps[:M]
+
+
+@pytest.mark.parametrize("M,K,seed", [(21, 512, 0), (16, 128, 1), (5, 1024, 2)])
+def test_hptq_blob_decodes_to_oracle_integers(M, K, seed):
+    enc = _hptq_enc(M, K, seed)
+    blob = qgemv.repack(enc)
+    q, steps = _decode_hptq_blob(blob)
+    assert np.array_equal(q, enc["q"])
+    assert np.array_equal(steps, enc["scales"].view(np.uint16))
+
+
+def test_hptq_validation():
+    INV, UNS = -1, -3
+    enc = _hptq_enc(4, 256)
+    assert _status(enc) == 0
+    bad = dict(enc); bad["row_bits"] = enc["row_bits"].copy(); bad["row_bits"][1] += 1
+    assert _status(bad) == INV                      # a row that does not hold exactly K codewords
+    bad = dict(enc); bad["huff_len"] = enc["huff_len"][::-1].copy()
+    assert _status(bad) == INV                      # lengths not canonical
+    bad = dict(enc); bad["huff_sym"] = enc["huff_sym"].copy(); bad["huff_sym"][0] = 4000
+    assert _status(bad) == INV                      # integer beyond 2048
+    bad = dict(enc); bad["group"] = 64
+    assert _status(bad) == UNS
+    bad = dict(enc); bad["K"] = 96
+    assert _status(bad) == UNS
+    s = enc["scales"].copy(); s[0, 0] = np.inf
+    bad = dict(enc); bad["scales"] = s
+    assert _status(bad) == INV
+    blob = qgemv.repack(enc)
+    out = np.zeros(4 * 256, np.uint8)
+    assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data) == UNS

@@ -379,3 +379,30 @@ def test_batched_rows_match_single(torch):
         _, A = gemv.gemv_rows(enc, x16[b:b + 1])
         assert np.all(np.abs(yb[b] - y1[0]) <= 2e-4 * A[0] + 2e-6)
     plan.close()
+
+
+# ---------------------------------------------------------------------------
+# HPTQ: prefix-coded integers on one grid (batch 1)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,bpw", [(64, 1024, 3.125), (33, 2048, 3.125), (21, 512, 2.5), (300, 256, 4.0)])
+def test_hptq_oracle_encoded(torch, M, K, bpw):
+    from oracle import hptq
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, M, K)
+    enc = hptq.encode(W, 128, bpw)
+    x16 = make_x(wl, 1, K, 0, M)
+    _say(f"[gpu] hptq M={M} K={K} bpw={enc['row_bits'][-1] / W.size:.3f} nsym={len(enc['huff_sym'])} "
+         f"maxlen={enc['huff_len'].max()}")
+    plan = qgemv.QGemv(enc)
+    y1 = run_b1(torch, plan, x16)
+    y_ref, A = hptq.gemv(enc, x16)
+    assert np.all(np.isfinite(y1)), "output not fully written"
+    ok, worst = gemv.within_tolerance(y1, y_ref, A)
+    assert ok, f"tolerance exceeded: worst {worst:.3f}"
+    y2 = run_b1(torch, plan, x16)
+    assert np.array_equal(y1, y2), "not bitwise deterministic"
+    xb = torch.zeros((8, K), dtype=torch.float16, device="cuda")
+    yb = torch.zeros((8, M), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert qgemv.lib().qgemv_run(plan._h, xb.data_ptr(), yb.data_ptr(), 8, s) == -3
+    plan.close()
