@@ -50,13 +50,18 @@ WORKLOAD_NOTES = {
                   "FP16 scale/zero per 16, 1% FP16 CSR outliers",
     "mlp7b_bpdq3": "MLP up-proj 11008x4096, 3-bit BPDQ codes + 4 FP16 bit-plane coefficients per row and group of "
                    "64, 0.45% FP16 CSR outliers",
+    "mlp7b_hptq": "MLP up-proj 11008x4096, HPTQ prefix-coded integers (about 3.2 bits per weight) on one grid with "
+                  "an FP16 step per row and group of 128, 0.45% outliers on the same grid",
 }
 DEFAULT_BATCH = {"block7b_u3": 16}
 
 
 def algorithmic_bytes(f: dict, B: int = 1) -> int:
-    M, K, bits = f["M"], f["K"], f["bits"]
+    M, K, bits = f["M"], f["K"], f.get("bits", 0)
     nnz = int(f["row_ptr"][-1])
+    if f["fmt"] == "hptq":  # stream, steps, row starts, the code's integers and lengths, x, y
+        return (int(f["row_bits"][-1]) + 7) // 8 + M * (K // f["group"]) * 2 + 8 * (M + 1) + \
+            3 * len(f["huff_sym"]) + 2 * B * K + 4 * B * M
     codes = M * K * bits // 8
     if f["fmt"] == "uniform":
         meta = M * (K // 16) * 4
@@ -262,7 +267,7 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": f"{a.workload}: {WORKLOAD_NOTES[a.workload]}, batch {B}", "batch": B,
-                   "bits": first["bits"], "format": first["fmt"], "layers": per_layer,
+                   "bits": first.get("bits", 0), "format": first["fmt"], "layers": per_layer,
                    "timing": "eager launches" if a.no_graph else "one HIP-graph replay of all steps per layer"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

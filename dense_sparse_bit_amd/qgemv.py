@@ -111,7 +111,7 @@ def make_weights(w: dict):
     s.M, s.K, s.bits, s.format = int(w["M"]), int(w["K"]), int(w.get("bits", 0)), fmt
     s.group_size = int(w.get("group", 16) or 16)
     s.nnz = int(w.get("nnz", nnz))
-    s.codes = ptr(w["codes_packed"] if "codes_packed" in w else w["stream"], np.uint8)
+    s.codes = ptr(w["stream"] if fmt == FMT["hptq"] else w["codes_packed"], np.uint8)
     s.scales = ptr(w.get("scales"), np.uint16)
     s.zeros = ptr(w.get("zeros"), np.uint16)
     s.lut = ptr(w.get("lut"), np.uint16)

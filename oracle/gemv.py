@@ -28,6 +28,10 @@ def decode_rows(enc: dict, rows=None, codes: np.ndarray | None = None) -> np.nda
         d_ij = C0 + sum_t C_t * bit_(t-1)(q_ij), coefficients of (row i, group j // group)
     Codes are read from the packed bitstream unless given.
     """
+    if enc["fmt"] == "hptq":
+        # [Babai/GPTQ] "3. Applications Pratiques et Algorithmes", HPTQ: d = s * q from the prefix-coded stream
+        from .hptq import decode_rows as hptq_rows
+        return hptq_rows(enc, rows)
     M, K, bits = enc["M"], enc["K"], enc["bits"]
     rows = np.arange(M) if rows is None else np.asarray(rows)
     if codes is None:

@@ -202,6 +202,21 @@ def encode(W16: np.ndarray, group: int = 128, bpw: float = 3.125, max_len: int =
             "values": np.zeros(0, np.float16)}
 
 
+def decode_rows(enc: dict, rows=None) -> np.ndarray:
+    """d = s * q for the given rows, read from the stream row by row (canonical
+    codewords rebuilt from the integers and lengths)."""
+    M, K = enc["M"], enc["K"]
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    sym, ln, codes = canonical_code(np.asarray(enc["huff_sym"], np.int64), np.asarray(enc["huff_len"], np.int64))
+    rb = np.asarray(enc["row_bits"], np.int64)
+    sub = np.stack([rb[rows], rb[rows + 1]], axis=1).ravel()
+    q = np.zeros((len(rows), K), dtype=np.int64)
+    for k, i in enumerate(rows):
+        q[k] = decode_stream(enc["stream"], rb[[i, i + 1]], K, sym, ln, codes)[0]
+    s = np.repeat(np.asarray(enc["scales"])[rows].astype(np.float64), enc["group"], axis=1)
+    return s * q
+
+
 def decode(enc: dict) -> np.ndarray:
     """d = s * q, q read back from the stream."""
     q = decode_stream(enc["stream"], enc["row_bits"], enc["K"], enc["huff_sym"], enc["huff_len"], enc["huff_code"])

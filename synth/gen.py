@@ -69,7 +69,49 @@ WORKLOADS = {
         6, "mlp7b_bpdq3",
         "MLP up-proj 11008x4096, 3-bit BPDQ variable grid (4 FP16 coefficients per row and group of 64), 0.45% outliers",
         11008, 4096, 3, "bpdq", 64, 0.0045, 0.02, "uniform_pos", (1, 8)),
+    "mlp7b_hptq": Workload(
+        7, "mlp7b_hptq",
+        "MLP up-proj 11008x4096, HPTQ: prefix-coded integers on one grid (FP16 step per row and group of 128), "
+        "about 3.2 bits per weight, 0.45% outliers on the same grid",
+        11008, 4096, 0, "hptq", 128, 0.0045, 0.02, "uniform_pos", (1,)),
 }
+
+# Synthetic prefix code for HPTQ storage-format inputs: integer length classes
+# 0 -> 2 bits, +-1 -> 3, +-2..3 -> 4, +-4..7 -> 6, +-8..15 -> 8, ..., +-128..255 -> 16.
+_HPTQ_CLASSES = [(0, 0, 2), (1, 1, 3), (2, 3, 4), (4, 7, 6), (8, 15, 8), (16, 31, 10), (32, 63, 12),
+                 (64, 127, 14), (128, 255, 16)]
+
+
+def hptq_synthetic_code():
+    """(integers, lengths, codewords) in canonical order: sorted by (length, integer);
+    each codeword is the previous plus 1, shifted left by the growth in length."""
+    sym, ln = [], []
+    for a, b, l in _HPTQ_CLASSES:
+        vals = [0] if a == 0 else list(range(-b, -a + 1)) + list(range(a, b + 1))
+        for v in vals:
+            sym.append(v); ln.append(l)
+    order = sorted(range(len(sym)), key=lambda k: (ln[k], sym[k]))
+    sym = np.array([sym[k] for k in order], dtype=np.int64)
+    ln = np.array([ln[k] for k in order], dtype=np.int64)
+    codes = np.zeros(len(sym), dtype=np.int64)
+    for k in range(1, len(sym)):
+        codes[k] = (codes[k - 1] + 1) << (ln[k] - ln[k - 1])
+    return sym, ln, codes
+
+
+def hptq_stream(q: np.ndarray, sym, ln, codes):
+    """Stream bytes (codewords most significant bit first, row by row) and row_bits [M+1]."""
+    M, K = q.shape
+    L = np.zeros(512, np.int64); C = np.zeros(512, np.int64)
+    L[sym + 256] = ln; C[sym + 256] = codes
+    lq = L[q.ravel() + 256]; cq = C[q.ravel() + 256]
+    start = np.cumsum(lq) - lq
+    row_bits = np.concatenate([[0], np.cumsum(lq.reshape(M, K).sum(axis=1))]).astype(np.int64)
+    bits = np.zeros(int(row_bits[-1] + 7) // 8 * 8, dtype=np.uint8)
+    for b in range(int(ln.max())):
+        m = lq > b
+        bits[start[m] + b] = ((cq[m] >> (lq[m] - 1 - b)) & 1).astype(np.uint8)
+    return np.packbits(bits), row_bits
 
 
 def workload(name: str) -> Workload:
@@ -228,6 +270,25 @@ def make_format_inputs(wl: Workload | str, layer: int = 0, M: int | None = None,
         G = K // wl.group
         out["scales"] = (rng.uniform(0.5, 1.5, size=(M, G)) * 4 * wl.sigma / (levels - 1)).astype(np.float16)
         out["zeros"] = rng.integers(0, levels, size=(M, G)).astype(np.float16)
+    elif wl.fmt == "hptq":
+        # integers rint(N(0, 1.5)) (|q| <= 255), steps ~ U(0.5, 1.5) * sigma / 1.5 per row and group of 128,
+        # and the outliers as large integers on the same grid
+        G = K // wl.group
+        q = np.clip(np.rint(rng.standard_normal((M, K)) * 1.5), -255, 255).astype(np.int64)
+        out["scales"] = (rng.uniform(0.5, 1.5, size=(M, G)) * wl.sigma / 1.5).astype(np.float16)
+        n = outlier_count(wl, M, K)
+        lin = np.sort(_rng(wl, layer, 1, M, K).choice(M * K, size=n, replace=False))
+        mag = _rng(wl, layer, 2, M, K).integers(32, 256, size=n)
+        q.ravel()[lin] = np.where(np.arange(n) % 2 == 0, mag, -mag)
+        sym, ln, codes = hptq_synthetic_code()
+        out["stream"], out["row_bits"] = hptq_stream(q, sym, ln, codes)
+        del out["codes_packed"]
+        out["huff_sym"] = sym.astype(np.int16)
+        out["huff_len"] = ln.astype(np.uint8)
+        out["q"] = q
+        out["rows"] = np.zeros(0, np.int64); out["cols"] = np.zeros(0, np.int64)
+        out["values"] = np.zeros(0, np.float16)
+        return out
     elif wl.fmt == "bpdq":
         G = K // wl.group
         c = np.empty((M, G, wl.bits + 1))

@@ -406,3 +406,17 @@ def test_hptq_oracle_encoded(torch, M, K, bpw):
     s = torch.cuda.current_stream().cuda_stream
     assert qgemv.lib().qgemv_run(plan._h, xb.data_ptr(), yb.data_ptr(), 8, s) == -3
     plan.close()
+
+
+def test_hptq_full_size_sampled(torch):
+    f = format_case("mlp7b_hptq")
+    M, K = f["M"], f["K"]
+    _say(f"[gpu] hptq full M={M} K={K} bits={f['row_bits'][-1]}")
+    x16 = make_x("mlp7b_hptq", 1, K, 0, M)
+    plan = qgemv.QGemv(f)
+    y = run_b1(torch, plan, x16)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.choice(M, size=160, replace=False)]))
+    check_y(y, dict(f, fmt="hptq"), x16, rows)
+    plan.close()

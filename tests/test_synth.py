@@ -65,3 +65,18 @@ def test_format_inputs_shapes():
     assert u["codes_packed"].shape == (4096, 11008 * 3 // 8) and u["scales"].shape == (4096, 688)
     z = u["zeros"].astype(np.float64)
     assert z.min() >= 0 and z.max() <= 7 and np.array_equal(z, np.rint(z))
+
+
+def test_hptq_format_inputs_are_whole_rows_of_codewords():
+    """The synthetic prefix code is a prefix code (Kraft sum <= 1), and the
+    stream holds exactly the drawn integers, K per row (read back by the oracle)."""
+    from oracle import hptq
+    sym, ln, codes = __import__("synth").hptq_synthetic_code()
+    assert sum(2.0 ** -int(l) for l in ln) <= 1.0
+    f = make_format_inputs("mlp7b_hptq", 0, 40, 512)
+    enc = dict(f, fmt="hptq")
+    q = hptq.decode_stream(f["stream"], f["row_bits"], 512, *hptq.canonical_code(
+        np.asarray(f["huff_sym"], np.int64), np.asarray(f["huff_len"], np.int64)))
+    assert np.array_equal(q, f["q"])
+    assert np.all(np.abs(f["q"]) <= 255)
+    assert 2.8 < f["row_bits"][-1] / f["q"].size < 3.6
