@@ -1248,9 +1248,12 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
 // sequence (qgemv_layout.h).  A wave copies a block's words into its own LDS
 // buffer; each lane keeps the next bits of its chunk in a 64-bit register
 // buffer, refilled from LDS every two codewords (a codeword has at most 16
-// bits), and looks the top 10 bits up in a 1024-entry table in LDS that
-// gives the integer and length of the codeword they start with; a longer
-// codeword is found from the canonical first codeword of each length.  The
+// bits), and looks the top 12 bits up in a 4096-entry table in LDS that
+// gives the integer and length of the codeword they start with.  A longer
+// codeword's length is the shortest l whose l-bit prefix lies below the end
+// of the canonical codewords of length l (compared without branches against
+// per-length limits held in scalar registers), and its integer one more LDS
+// read.  The
 // integers are exact in FP16 and form the A operand of four MFMAs against x;
 // each row's step scales the block's sums in fp32.  The blocks of a
 // workgroup are cut into 16 runs, one per wave, with a partial slot per
@@ -1275,19 +1278,30 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   const int L = TW * nkb;
   const int b0 = w * L / kWaves, b1 = (w + 1) * L / kWaves;  // this wave's run
 
-  // LDS: xs [K] FP16 | table [1024] | first, count, offset [3][17] (+1) | integers [nsym] int16 (padded)
-  //      | slots [TW+15][16] | code buffers [16][kHuffBufWords]
+  // LDS: xs [K] FP16 | table [kHuffTable] | integers [nsym] int16 (padded) | slots [TW+15][16]
+  //      | code buffers [16][kHuffBufWords]
   uint16_t* xs = (uint16_t*)lds;
   int32_t* tab = (int32_t*)(lds + K / 2);
-  int32_t* slow = tab + kHuffTable;
-  int16_t* syms = (int16_t*)(slow + 52);
-  float* slots = (float*)(slow + 52 + ((nsym + 1) / 2 + 3) / 4 * 4);
+  int16_t* syms = (int16_t*)(tab + kHuffTable);
+  float* slots = (float*)(tab + kHuffTable + ((nsym + 1) / 2 + 3) / 4 * 4);
   uint32_t* buf = (uint32_t*)(slots + (TW + 15) * 16) + w * kHuffBufWords;
 
   for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
-  for (int i = threadIdx.x; i < kHuffTable + 51; i += 64 * kWaves) tab[i] = htab[i];
+  for (int i = threadIdx.x; i < kHuffTable / 4; i += 64 * kWaves) ((u32x4_t*)tab)[i] = ((const u32x4_t*)htab)[i];
   for (int i = threadIdx.x; i < nsym; i += 64 * kWaves) syms[i] = hsym[i];
 
+  // Canonical codewords longer than the table index (lengths kHuffBits+1 .. 16):
+  // per length the first codeword, the end of the range and the index of the first in syms.
+  constexpr int NL = kHuffMaxLen - kHuffBits;
+  uint32_t lfirst[NL], llimit[NL];
+  int loff[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int l = kHuffBits + 1 + k;
+    lfirst[k] = (uint32_t)htab[kHuffTable + l];
+    llimit[k] = lfirst[k] + (uint32_t)htab[kHuffTable + 17 + l];
+    loff[k] = htab[kHuffTable + 34 + l];
+  }
   const rsrc_t rw = make_rsrc(words, nwords * 4u);
   u32x4_t pre = {0u, 0u, 0u, 0u};
   uint32_t lbn = 0, stn0 = 0, stn1 = 0;
@@ -1354,14 +1368,19 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
           int len = e & 255;
           int32_t q = e >> 8;
           if (len == 0) {  // a codeword longer than the table's index
-            for (int l = kHuffBits + 1; l <= kHuffMaxLen; ++l) {
-              const uint32_t c = win >> (32 - l);
-              if (c - (uint32_t)slow[l] < (uint32_t)slow[17 + l]) {
-                q = syms[slow[34 + l] + (int)(c - (uint32_t)slow[l])];
-                len = l;
-                break;
-              }
+            uint32_t f = lfirst[NL - 1], c = win >> (32 - kHuffMaxLen);
+            int o = loff[NL - 1];
+            len = kHuffMaxLen;
+#pragma unroll
+            for (int k = NL - 2; k >= 0; --k) {  // the shortest length whose range the prefix falls in
+              const uint32_t ck = win >> (32 - (kHuffBits + 1 + k));
+              const bool in = ck < llimit[k];
+              len = in ? kHuffBits + 1 + k : len;
+              f = in ? lfirst[k] : f;
+              o = in ? loff[k] : o;
+              c = in ? ck : c;
             }
+            q = syms[min(o + (int)(c - f), nsym - 1)];
           }
           bits <<= len;
           nb -= len;
@@ -1635,7 +1654,7 @@ hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   const BlobHeader& h = p->h;
   const int grid = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-  size_t lds = (size_t)h.K * 2 + (size_t)(kHuffTable + 52) * 4 + (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4 +
+  size_t lds = (size_t)h.K * 2 + (size_t)kHuffTable * 4 + (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4 +
                (tw + 15) * 16 * 4 + (size_t)kWaves * kHuffBufWords * 4;
   if (lds > kLdsBytes) return hipErrorInvalidValue;
   if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;

@@ -52,8 +52,8 @@
 //         HPTQ: per (tile, K-block) the 16 rows' FP16 steps (group 128 = the
 //         K-block).
 // hidx    HPTQ: uint32 [tiles*nkb + 1]; hlane: uint16 [tiles*nkb*64];
-// htab    HPTQ: int32 [1024]: for the next 10 bits of a chunk, (q << 8) | len
-//         of the codeword they start with if len <= 10, else 0; then int32
+// htab    HPTQ: int32 [4096]: for the next 12 bits of a chunk, (q << 8) | len
+//         of the codeword they start with if len <= 12, else 0; then int32
 //         [3][17]: per length l the first canonical codeword, the number of
 //         codewords and the index of the first in hsym.
 // hsym    HPTQ: int16 [hsym]: the codewords' integers in canonical order.
@@ -78,14 +78,14 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 5;
+constexpr uint32_t kVersion = 6;
 constexpr int kTileRows = 16;
 constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
 constexpr int kMaxK = 16384;
 constexpr uint64_t kAlign = 256;
 constexpr uint64_t kHeaderBytes = 256;
-constexpr int kHuffBits = 10;               // HPTQ decode table index: the next 10 bits
+constexpr int kHuffBits = 12;               // HPTQ decode table index: the next 12 bits
 constexpr int kHuffTable = 1 << kHuffBits;
 constexpr int kHuffMaxLen = 16;
 constexpr int kHuffMaxSym = 4096;

@@ -270,8 +270,10 @@ def _decode_hptq_blob(blob):
     words = blob[off_codes:off_codes + 4 * int(hidx[-1]) + 8].view(np.uint32)
     words = np.concatenate([words, np.zeros(2, np.uint32)])
     hlane = blob[off_hlane:off_hlane + 2 * 64 * tiles * nkb].view(np.uint16)
-    tab = blob[off_htab:off_htab + 4 * (1024 + 51)].view(np.int32)
-    first, count, offs = tab[1024:1041], tab[1041:1058], tab[1058:1075]
+    tbits = 12
+    nt = 1 << tbits
+    tab = blob[off_htab:off_htab + 4 * (nt + 51)].view(np.int32)
+    first, count, offs = tab[nt:nt + 17], tab[nt + 17:nt + 34], tab[nt + 34:nt + 51]
     syms = blob[off_hsym:off_hsym + 2 * nsym].view(np.int16)
     q = np.zeros((tiles * 16, nkb * 128), dtype=np.int64)
     for blk in range(tiles * nkb):
@@ -284,11 +286,11 @@ def _decode_hptq_blob(blob):
             for j in range(32):
                 w0, w1 = int(words[p >> 5]), int(words[(p >> 5) + 1])
                 win = ((w0 << 32 | w1) >> (32 - (p & 31))) & 0xFFFFFFFF
-                e = int(tab[win >> 22])
+                e = int(tab[win >> (32 - tbits)])
                 if e & 255:
                     ln, v = e & 255, e >> 8
                 else:
-                    for ln in range(11, 17):
+                    for ln in range(tbits + 1, 17):
                         c = win >> (32 - ln)
                         if count[ln] and first[ln] <= c < first[ln] + count[ln]:
                             v = int(syms[offs[ln] + c - first[ln]])
