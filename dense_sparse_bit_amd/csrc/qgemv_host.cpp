@@ -16,6 +16,17 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// IEEE binary16 bits of an integer of magnitude at most 2048 (exact).
+uint16_t int_to_half(int v) {
+  const uint32_t sign = v < 0 ? 0x8000u : 0u;
+  uint32_t m = (uint32_t)(v < 0 ? -v : v);
+  if (m == 0) return (uint16_t)sign;
+  int e = 0;
+  while ((m >> (e + 1)) != 0) ++e;  // m = 1.f * 2^e
+  const uint32_t man = e <= 10 ? (m << (10 - e)) & 1023u : (m >> (e - 10)) & 1023u;
+  return (uint16_t)(sign | ((uint32_t)(e + 15) << 10) | man);
+}
+
 // IEEE binary16 bits -> float.
 float half_to_float(uint16_t h) {
   const uint32_t sign = (uint32_t)(h >> 15) << 31;
@@ -214,6 +225,20 @@ struct HuffCode {
   int first[kHuffMaxLen + 1], count[kHuffMaxLen + 1], offset[kHuffMaxLen + 1];
 };
 
+// Number of distinct kHuffBits-bit prefixes among codewords longer than kHuffBits.
+static uint32_t hptq_nsub(const qgemv_weights* w, const HuffCode& hc) {
+  uint32_t n = 0;
+  int64_t last = -1;
+  for (int k = 0; k < w->huff_nsym; ++k) {  // canonical order: prefixes ascend
+    const int l = w->huff_len[k];
+    if (l <= kHuffBits) continue;
+    const int64_t pre = hc.code[k] >> (l - kHuffBits);
+    if (pre != last) ++n;
+    last = pre;
+  }
+  return n;
+}
+
 static int hptq_code(const qgemv_weights* w, HuffCode& hc) {
   const int n = w->huff_nsym;
   if (!w->huff_len || !w->huff_sym) return QGEMV_ERR_INVALID_ARG;
@@ -272,11 +297,12 @@ static int hptq_decode(const qgemv_weights* w, const HuffCode& hc, std::vector<i
 
 // Words of the HPTQ code section: every block's chunks, padded to 16 bytes.
 static uint64_t hptq_words(const qgemv_weights* w, const HuffCode& hc, const std::vector<int16_t>& q,
-                           std::vector<uint32_t>* hidx) {
+                           std::vector<uint32_t>* hidx, uint32_t* maxw) {
   const int M = w->M, K = w->K, nkb = K / kBlockK, tiles = (M + kTileRows - 1) / kTileRows;
   std::vector<int> len_of(4097, 0);
   for (int k = 0; k < w->huff_nsym; ++k) len_of[w->huff_sym[k] + 2048] = w->huff_len[k];
   uint64_t words = 0;
+  *maxw = 0;
   if (hidx) hidx->assign((size_t)tiles * nkb + 1, 0);
   for (int t = 0; t < tiles; ++t)
     for (int b = 0; b < nkb; ++b) {
@@ -287,7 +313,9 @@ static uint64_t hptq_words(const qgemv_weights* w, const HuffCode& hc, const std
         if (row >= M) continue;
         for (int j = 0; j < kBlockK; ++j) bits += len_of[q[(size_t)row * K + b * kBlockK + j] + 2048];
       }
-      words += ((bits + 31) / 32 + 3) / 4 * 4;
+      const uint64_t bw = ((bits + 31) / 32 + 3) / 4 * 4;
+      if (bw > *maxw) *maxw = (uint32_t)bw;
+      words += bw;
     }
   if (hidx) (*hidx)[(size_t)tiles * nkb] = (uint32_t)words;
   return words;
@@ -355,19 +383,20 @@ static int header_of(const qgemv_weights* w, BlobHeader& h, HuffCode* hc_out = n
                      std::vector<int16_t>* q_out = nullptr) {
   int st = validate_arrays(w);
   if (st) return st;
-  uint32_t words = 0;
+  uint32_t words = 0, maxw = 0, nsub = 0;
   if (w->format == QGEMV_FMT_HPTQ) {
     HuffCode hc;
     std::vector<int16_t> q;
     if ((st = hptq_code(w, hc))) return st;
+    nsub = hptq_nsub(w, hc);
     if ((st = hptq_decode(w, hc, q))) return st;
-    const uint64_t nw = hptq_words(w, hc, q, nullptr);
+    const uint64_t nw = hptq_words(w, hc, q, nullptr, &maxw);
     if (nw >= ((uint64_t)1 << 29)) return QGEMV_ERR_UNSUPPORTED;
     words = (uint32_t)nw;
     if (hc_out) *hc_out = hc;
     if (q_out) q_out->swap(q);
   }
-  h = make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz, w->huff_nsym, words);
+  h = make_header(w->M, w->K, w->bits, w->format, w->group_size, w->nnz, w->huff_nsym, words, maxw, nsub);
   if (h.total_bytes >= ((uint64_t)1 << 31)) return QGEMV_ERR_UNSUPPORTED;
   return QGEMV_OK;
 }
@@ -408,7 +437,8 @@ static int repack_hptq(const qgemv_weights* w, void* dst_host, size_t bytes) {
     cl[w->huff_sym[k] + 2048] = w->huff_len[k];
   }
   std::vector<uint32_t> hidx;
-  hptq_words(w, hc, q, &hidx);
+  uint32_t maxw;
+  hptq_words(w, hc, q, &hidx, &maxw);
   uint32_t* words = (uint32_t*)(blob + h.off_codes);
   uint16_t* hlane = (uint16_t*)(blob + h.off_hlane);
   uint16_t* steps = (uint16_t*)(blob + h.off_meta);
@@ -434,18 +464,36 @@ static int repack_hptq(const qgemv_weights* w, void* dst_host, size_t bytes) {
     }
   std::memcpy(blob + h.off_hidx, hidx.data(), 4 * hidx.size());
   int32_t* tab = (int32_t*)(blob + h.off_htab);
+  int32_t* sub = tab + kHuffTable + 4 * 17;
+  constexpr int kSubBits = kHuffMaxLen - kHuffBits;
+  for (uint32_t i = 0; i < 16u * h.hsub; ++i) sub[i] = kHuffMaxLen;
+  int64_t last = -1;
+  int nsub = -1;
   for (int k = 0; k < n; ++k) {
     const int l = w->huff_len[k];
-    if (l > kHuffBits) continue;
-    const int32_t e = (int32_t)((uint32_t)(int32_t)w->huff_sym[k] << 8) | l;
-    const uint32_t lo = hc.code[k] << (kHuffBits - l);
-    for (uint32_t s = 0; s < (1u << (kHuffBits - l)); ++s) tab[lo + s] = e;
+    const uint32_t e = ((uint32_t)int_to_half(w->huff_sym[k]) << 16) | (uint32_t)l;
+    if (l <= kHuffBits) {
+      const uint32_t lo = hc.code[k] << (kHuffBits - l);
+      for (uint32_t s = 0; s < (1u << (kHuffBits - l)); ++s) tab[lo + s] = (int32_t)e;
+      continue;
+    }
+    const uint32_t pre = hc.code[k] >> (l - kHuffBits);
+    if ((int64_t)pre != last) {
+      ++nsub;
+      last = pre;
+      tab[pre] = (int32_t)((uint32_t)(16 * nsub) << 16);
+    }
+    const uint32_t lo = (hc.code[k] << (kHuffMaxLen - l)) & ((1u << kSubBits) - 1);
+    for (uint32_t s = 0; s < (1u << (kHuffMaxLen - l)); ++s) sub[16 * nsub + lo + s] = (int32_t)e;
   }
   int32_t* slow = tab + kHuffTable;
+  int32_t lim = 0;
   for (int l = 0; l <= kHuffMaxLen; ++l) {
     slow[l] = hc.first[l];
     slow[17 + l] = hc.count[l];
     slow[34 + l] = hc.offset[l];
+    if (hc.count[l]) lim = (hc.first[l] + hc.count[l]) << (kHuffMaxLen - l);
+    slow[51 + l] = lim;
   }
   std::memcpy(blob + h.off_hsym, w->huff_sym, 2 * (size_t)n);
   return QGEMV_OK;

@@ -1245,29 +1245,51 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
 // HPTQ, batch 1: prefix-coded integers on one grid.
 //
 // A (tile, K-block) block holds its 64 lanes' 32-codeword chunks as one bit
-// sequence (qgemv_layout.h).  A wave copies a block's words into its own LDS
-// buffer; each lane keeps the next bits of its chunk in a 64-bit register
-// buffer, refilled from LDS every two codewords (a codeword has at most 16
-// bits), and looks the top 12 bits up in a 4096-entry table in LDS that
-// gives the integer and length of the codeword they start with.  A longer
-// codeword's length is the shortest l whose l-bit prefix lies below the end
-// of the canonical codewords of length l (compared without branches against
-// per-length limits held in scalar registers), and its integer one more LDS
-// read.  The
-// integers are exact in FP16 and form the A operand of four MFMAs against x;
-// each row's step scales the block's sums in fp32.  The blocks of a
-// workgroup are cut into 16 runs, one per wave, with a partial slot per
-// (wave, tile) as in k_xlds, and the outputs add the slots in wave order.
-// The next block's first 1 KiB of code words, lane offset and steps are
-// loaded while the current block is decoded.
+// sequence (qgemv_layout.h).  A wave takes the blocks of its run G at a
+// time: it copies their words into G LDS buffers and decodes the G chunks of
+// each lane side by side, so that the G chains of dependent table reads hide
+// one another's latency.  Each chain keeps the next bits of its chunk in a
+// 64-bit register, refilled from LDS every two codewords (a codeword has at
+// most 16 bits), and looks its top 12 bits up in a 4096-entry table in LDS
+// that gives the FP16 integer and the length of the codeword they start
+// with.  A longer codeword's length is the shortest l whose 16-bit
+// left-justified prefix lies below the end of the canonical codewords of
+// length l (compared without branches against limits held in scalar
+// registers), and its integer one more LDS read.  The integers are exact in
+// FP16 and form the A operand of four MFMAs against x; each row's step
+// scales the block's sums in fp32.  The blocks of a workgroup are cut into
+// 16 runs, one per wave, with a partial slot per (wave, tile) as in k_xlds,
+// and the outputs add the slots in wave order.  The next G blocks' first
+// 1 KiB of code words, lane offsets and steps are loaded while the current
+// ones are decoded.
 // ---------------------------------------------------------------------------
-constexpr int kHuffBufWords = 1024 + 8;  // a block's largest code (64 * 32 * 16 bits) and a spill
+constexpr int kHuffMaxBlockWords = 64 * kChunkCodes * kHuffMaxLen / 32;  // a block's largest code
+constexpr int kHuffPad = 20;  // words a chain may read past its chunk's start word, and past the block
+constexpr int kHuffMaxSub = 512;  // second-level tables held in LDS (32 KiB)
 
+static_assert(kHuffMaxLen - kHuffBits == 4, "huff_long compares four lengths");
+__device__ __forceinline__ uint32_t huff_long(uint32_t win, uint32_t l0, uint32_t l1, uint32_t l2, int d0, int d1,
+                                              int d2, int d3, const uint16_t* syms, int nsym) {
+  // lengths 13 .. 16: the shortest whose codewords end above the prefix
+  const uint32_t p16 = win >> (32 - kHuffMaxLen);
+  uint32_t len = 16;
+  int d = d3;
+  len = p16 < l2 ? 15u : len;
+  d = p16 < l2 ? d2 : d;
+  len = p16 < l1 ? 14u : len;
+  d = p16 < l1 ? d1 : d;
+  len = p16 < l0 ? 13u : len;
+  d = p16 < l0 ? d0 : d;
+  const uint32_t idx = min((uint32_t)((int)(p16 >> (kHuffMaxLen - len)) + d), (uint32_t)(nsym - 1));
+  return ((uint32_t)syms[idx] << 16) | len;
+}
+
+template <int G, bool SUB>
 __global__ void __launch_bounds__(64 * kWaves)
 k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, const uint32_t* __restrict__ hidx,
        const uint16_t* __restrict__ hlane, const int32_t* __restrict__ htab, const int16_t* __restrict__ hsym,
        const uint16_t* __restrict__ x, float* __restrict__ y, int M, int K, int nkb, int tiles, int nsym,
-       uint32_t nwords) {
+       uint32_t nwords, int bufw, int nsub) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1278,42 +1300,57 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   const int L = TW * nkb;
   const int b0 = w * L / kWaves, b1 = (w + 1) * L / kWaves;  // this wave's run
 
-  // LDS: xs [K] FP16 | table [kHuffTable] | integers [nsym] int16 (padded) | slots [TW+15][16]
-  //      | code buffers [16][kHuffBufWords]
+  // LDS: table [kHuffTable] (static, at address 0) | xs [K] FP16 | aux | slots [TW+15][16]
+  //      | code buffers [16][G][bufw]; aux: the second-level tables [max(nsub, 1)][16]
+  //      (SUB), else the integers [nsym] FP16 (padded)
+  __shared__ int32_t tab[kHuffTable];
   uint16_t* xs = (uint16_t*)lds;
-  int32_t* tab = (int32_t*)(lds + K / 2);
-  int16_t* syms = (int16_t*)(tab + kHuffTable);
-  float* slots = (float*)(tab + kHuffTable + ((nsym + 1) / 2 + 3) / 4 * 4);
-  uint32_t* buf = (uint32_t*)(slots + (TW + 15) * 16) + w * kHuffBufWords;
+  uint32_t* aux = lds + K / 2;
+  uint16_t* syms = (uint16_t*)aux;
+  const int auxw = SUB ? 16 * max(nsub, 1) : ((nsym + 1) / 2 + 3) / 4 * 4;
+  float* slots = (float*)(aux + auxw);
+  const int bofs = K / 2 + auxw + (TW + 15) * 16 + w * G * bufw;  // in lds, in words
+  uint32_t* buf = lds + bofs;
 
   for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
   for (int i = threadIdx.x; i < kHuffTable / 4; i += 64 * kWaves) ((u32x4_t*)tab)[i] = ((const u32x4_t*)htab)[i];
-  for (int i = threadIdx.x; i < nsym; i += 64 * kWaves) syms[i] = hsym[i];
-
-  // Canonical codewords longer than the table index (lengths kHuffBits+1 .. 16):
-  // per length the first codeword, the end of the range and the index of the first in syms.
-  constexpr int NL = kHuffMaxLen - kHuffBits;
-  uint32_t lfirst[NL], llimit[NL];
-  int loff[NL];
-#pragma unroll
-  for (int k = 0; k < NL; ++k) {
-    const int l = kHuffBits + 1 + k;
-    lfirst[k] = (uint32_t)htab[kHuffTable + l];
-    llimit[k] = lfirst[k] + (uint32_t)htab[kHuffTable + 17 + l];
-    loff[k] = htab[kHuffTable + 34 + l];
+  if (SUB) {
+    const u32x4_t* src = (const u32x4_t*)(htab + kHuffTable + 4 * 17);
+    for (int i = threadIdx.x; i < 4 * nsub; i += 64 * kWaves) ((u32x4_t*)aux)[i] = src[i];
+  } else {
+    for (int i = threadIdx.x; i < nsym; i += 64 * kWaves)
+      syms[i] = __builtin_bit_cast(uint16_t, (_Float16)(float)hsym[i]);
   }
+
+  // Codewords longer than the table index, lengths 13 .. 16: the
+  // left-justified end of each length's codewords, and the index in syms of
+  // a codeword c of that length minus c.
+  const int32_t* lj = htab + kHuffTable + 51;
+  const int32_t* fi = htab + kHuffTable;
+  const int32_t* of = htab + kHuffTable + 34;
+  const uint32_t l13 = (uint32_t)lj[13], l14 = (uint32_t)lj[14], l15 = (uint32_t)lj[15];
+  const int d13 = of[13] - fi[13], d14 = of[14] - fi[14], d15 = of[15] - fi[15], d16 = of[16] - fi[16];
   const rsrc_t rw = make_rsrc(words, nwords * 4u);
-  u32x4_t pre = {0u, 0u, 0u, 0u};
-  uint32_t lbn = 0, stn0 = 0, stn1 = 0;
-  auto prefetch = [&](int bb) {  // first 1 KiB of block bb's words, lane offset, steps of rows 4*(lane/16) .. +3
-    if (bb < b1) {
-      const int g = T0 * nkb + bb;
-      const uint32_t wo = hidx[g];
-      pre = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + 4u * (uint32_t)lane) * 4u), 0, kNonTemporal);
-      lbn = hlane[(size_t)g * 64 + lane];
-      const uint32_t* sp = (const uint32_t*)(steps + (size_t)g * 16 + 4 * (lane >> 4));
-      stn0 = sp[0];
-      stn1 = sp[1];
+  u32x4_t pre[G];
+  uint32_t lbn[G], stn0[G], stn1[G];
+#pragma unroll
+  for (int c = 0; c < G; ++c) {
+    pre[c] = (u32x4_t){0u, 0u, 0u, 0u};
+    lbn[c] = stn0[c] = stn1[c] = 0u;
+  }
+  auto prefetch = [&](int r0) {  // per block: first 1 KiB of words, lane offset, steps of rows 4*(lane/16) .. +3
+#pragma unroll
+    for (int c = 0; c < G; ++c) {
+      const int bb = r0 + c;
+      if (bb < b1) {
+        const int g = T0 * nkb + bb;
+        const uint32_t wo = hidx[g];
+        pre[c] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + 4u * (uint32_t)lane) * 4u), 0, kNonTemporal);
+        lbn[c] = hlane[(size_t)g * 64 + lane];
+        const uint32_t* sp = (const uint32_t*)(steps + (size_t)g * 16 + 4 * (lane >> 4));
+        stn0[c] = sp[0];
+        stn1[c] = sp[1];
+      }
     }
   };
   prefetch(b0);
@@ -1327,82 +1364,95 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       for (int i = 0; i < 4; ++i) slots[(w + tl) * 16 + 4 * (lane >> 4) + i] = acc[i];
   };
   const int sl = 32 * (lane >> 4);
-  for (int bb = b0; bb < b1; ++bb) {
-    const int t = bb / nkb, kb = bb - t * nkb;
-    if (t != tl) {
-      flush();
-      acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-      tl = t;
-    }
-    const int g = T0 * nkb + bb;
-    const uint32_t wo = hidx[g], nw = hidx[g + 1] - wo;  // a multiple of 4
-    // the block's words into this wave's buffer: the first 1 KiB from the prefetch, any more now
-    if (4 * lane < (int)nw) ((u32x4_t*)buf)[lane] = pre;
-    for (uint32_t i = 256u + 4u * (uint32_t)lane; i < nw; i += 256u)
-      *(u32x4_t*)(buf + i) = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + i) * 4u), 0, kNonTemporal);
-    if (lane < 2) buf[nw + lane] = 0u;
-    const uint32_t lb = lbn, st0 = stn0, st1 = stn1;
-    prefetch(bb + 1);
-
-    // decode this lane's 32 codewords
-    uint32_t qh[16];
-    const bool real = T0 * 16 + t * 16 + (lane & 15) < M;
-    if (real) {
-      uint32_t wi = (lb >> 5) + 2;
-      const uint32_t s0 = lb & 31u;
-      uint64_t bits = (((uint64_t)buf[lb >> 5] << 32) | buf[(lb >> 5) + 1]) << s0;
-      int nb = 64 - (int)s0;
+  const uint32_t cap = (uint32_t)(bufw - kHuffPad);
+  for (int r0 = b0; r0 < b1; r0 += G) {
+    uint32_t lb[G], st0[G], st1[G];
 #pragma unroll
-      for (int j = 0; j < 32; j += 2) {
-        const uint32_t nxt = buf[wi];
-        if (nb < 32) {  // two codewords always fit after a refill
-          bits |= (uint64_t)nxt << (32 - nb);
-          nb += 32;
-          ++wi;
-        }
-        int32_t q2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint32_t win = (uint32_t)(bits >> 32);
-          const int32_t e = tab[win >> (32 - kHuffBits)];
-          int len = e & 255;
-          int32_t q = e >> 8;
-          if (len == 0) {  // a codeword longer than the table's index
-            uint32_t f = lfirst[NL - 1], c = win >> (32 - kHuffMaxLen);
-            int o = loff[NL - 1];
-            len = kHuffMaxLen;
-#pragma unroll
-            for (int k = NL - 2; k >= 0; --k) {  // the shortest length whose range the prefix falls in
-              const uint32_t ck = win >> (32 - (kHuffBits + 1 + k));
-              const bool in = ck < llimit[k];
-              len = in ? kHuffBits + 1 + k : len;
-              f = in ? lfirst[k] : f;
-              o = in ? loff[k] : o;
-              c = in ? ck : c;
-            }
-            q = syms[min(o + (int)(c - f), nsym - 1)];
-          }
-          bits <<= len;
-          nb -= len;
-          q2[u] = q;
-        }
-        const _Float16 h0 = (_Float16)(float)q2[0], h1 = (_Float16)(float)q2[1];
-        qh[j / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    for (int c = 0; c < G; ++c) {
+      const int bb = r0 + c;
+      uint32_t* bc = buf + c * bufw;
+      lb[c] = 0u;
+      if (bb < b1) {
+        const int t = bb / nkb;
+        const int g = T0 * nkb + bb;
+        const uint32_t wo = hidx[g], nw = min(hidx[g + 1] - wo, cap);  // a multiple of 4
+        // the block's words: the first 1 KiB from the prefetch, any more now
+        if (4 * lane < (int)nw) ((u32x4_t*)bc)[lane] = pre[c];
+        for (uint32_t i = 256u + 4u * (uint32_t)lane; i < nw; i += 256u)
+          *(u32x4_t*)(bc + i) = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + i) * 4u), 0, kNonTemporal);
+        if (T0 * 16 + t * 16 + (lane & 15) < M) lb[c] = min(lbn[c], 32u * cap);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) qh[j] = 0u;
+      st0[c] = stn0[c];
+      st1[c] = stn1[c];
     }
-    floatx4_t blk = {0.f, 0.f, 0.f, 0.f};
+    prefetch(r0 + G);
+
+    // decode the G chunks of this lane, 32 codewords each, side by side; every
+    // 8 codewords of a chunk are one MFMA A operand.  Each pair of codewords
+    // (at most 32 bits) is the 32-bit window at the chunk's bit position: with
+    // p = position + 31, the words p/32 - 1 and p/32 funnel-shifted right by
+    // -position mod 32.  Rows past M decode whatever their lanes read; their
+    // sums are never stored.
+    uint32_t qh[G][4];
+    floatx4_t blk[G];
+    uint32_t p[G];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const half8_t bx = *(const half8_t*)(xs + kb * kBlockK + sl + 8 * i);
-      blk = mfma(h8(qh[4 * i], qh[4 * i + 1], qh[4 * i + 2], qh[4 * i + 3]), bx, blk);
+    for (int c = 0; c < G; ++c) {
+      blk[c] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+      p[c] = lb[c] + 31u;
     }
-    acc[0] += (float)__builtin_bit_cast(_Float16, (uint16_t)st0) * blk[0];
-    acc[1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(st0 >> 16)) * blk[1];
-    acc[2] += (float)__builtin_bit_cast(_Float16, (uint16_t)st1) * blk[2];
-    acc[3] += (float)__builtin_bit_cast(_Float16, (uint16_t)(st1 >> 16)) * blk[3];
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) {
+      uint32_t win[G], e[2][G];
+#pragma unroll
+      for (int c = 0; c < G; ++c) {
+        const uint32_t k = (uint32_t)(bofs + c * bufw - 1) + (p[c] >> 5);
+        win[c] = __builtin_amdgcn_alignbit(lds[k], lds[k + 1], ~p[c]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int c = 0; c < G; ++c) e[u][c] = (uint32_t)tab[win[c] >> (32 - kHuffBits)];
+#pragma unroll
+        for (int c = 0; c < G; ++c)
+          if ((e[u][c] & 255u) == 0u) {
+            if (SUB)  // the second-level table of these 12 bits, indexed by the next 4
+              e[u][c] = aux[(e[u][c] >> 16) + ((win[c] >> (32 - kHuffMaxLen)) & 15u)];
+            else
+              e[u][c] = huff_long(win[c], l13, l14, l15, d13, d14, d15, d16, syms, nsym);
+          }
+        if (u == 0)
+#pragma unroll
+          for (int c = 0; c < G; ++c) win[c] <<= (e[0][c] & 31u);
+      }
+#pragma unroll
+      for (int c = 0; c < G; ++c) {
+        p[c] += (e[0][c] & 0xffffu) + (e[1][c] & 0xffffu);
+        qh[c][(j / 2) & 3] = __builtin_amdgcn_perm(e[1][c], e[0][c], 0x07060302u);
+        if ((j & 7) == 6) {
+          const int bb = r0 + c, kb = bb - (bb / nkb) * nkb;
+          const half8_t bx = *(const half8_t*)(xs + kb * kBlockK + sl + j - 6);
+          blk[c] = mfma(h8(qh[c][0], qh[c][1], qh[c][2], qh[c][3]), bx, blk[c]);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int c = 0; c < G; ++c) {
+      const int bb = r0 + c;
+      if (bb < b1) {
+        const int t = bb / nkb;
+        if (t != tl) {
+          flush();
+          acc = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+          tl = t;
+        }
+        acc[0] += (float)__builtin_bit_cast(_Float16, (uint16_t)st0[c]) * blk[c][0];
+        acc[1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(st0[c] >> 16)) * blk[c][1];
+        acc[2] += (float)__builtin_bit_cast(_Float16, (uint16_t)st1[c]) * blk[c][2];
+        acc[3] += (float)__builtin_bit_cast(_Float16, (uint16_t)(st1[c] >> 16)) * blk[c][3];
+      }
+    }
   }
   if (b0 < b1) flush();
   __syncthreads();
@@ -1649,23 +1699,48 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   return hipGetLastError();
 }
 
-// HPTQ, batch 1: one workgroup per CU over its tile range.
+// HPTQ, batch 1: one workgroup per CU over its tile range; G = 2 blocks
+// decoded side by side per wave where their buffers fit in LDS, else one.
+// Long codewords go through the second-level tables where they fit in LDS,
+// else through the canonical search.
+template <int G, bool SUB>
+hipError_t launch_huff_g(const qgemv_plan* p, const uint16_t* x, float* y, int grid, size_t lds, int bufw,
+                         hipStream_t st) {
+  const BlobHeader& h = p->h;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_huff<G, SUB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)(kLdsBytes - (size_t)kHuffTable * 4));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((k_huff<G, SUB>), dim3(grid), dim3(64 * kWaves), lds, st,
+                     (const uint32_t*)(p->blob + h.off_codes), (const uint16_t*)(p->blob + h.off_meta),
+                     (const uint32_t*)(p->blob + h.off_hidx), (const uint16_t*)(p->blob + h.off_hlane),
+                     (const int32_t*)(p->blob + h.off_htab), (const int16_t*)(p->blob + h.off_hsym), x, y, h.M, h.K,
+                     h.nkb, h.tiles, h.hsym, h.hwords, bufw, (int)h.hsub);
+  return hipGetLastError();
+}
+
 hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
   const BlobHeader& h = p->h;
   const int grid = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-  size_t lds = (size_t)h.K * 2 + (size_t)kHuffTable * 4 + (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4 +
-               (tw + 15) * 16 * 4 + (size_t)kWaves * kHuffBufWords * 4;
-  if (lds > kLdsBytes) return hipErrorInvalidValue;
-  if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_huff, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(k_huff, dim3(grid), dim3(64 * kWaves), lds, st, (const uint32_t*)(p->blob + h.off_codes),
-                     (const uint16_t*)(p->blob + h.off_meta), (const uint32_t*)(p->blob + h.off_hidx),
-                     (const uint16_t*)(p->blob + h.off_hlane), (const int32_t*)(p->blob + h.off_htab),
-                     (const int16_t*)(p->blob + h.off_hsym), x, y, h.M, h.K, h.nkb, h.tiles, h.hsym, h.hwords);
-  return hipGetLastError();
+  const int bufw = (int)((h.hmaxw + kHuffPad + 3) / 4 * 4);
+  const size_t table = (size_t)kHuffTable * 4;  // static LDS
+  for (int sub = 1; sub >= 0; --sub) {
+    const size_t aux = sub ? (size_t)16 * (h.hsub > 1 ? h.hsub : 1) * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
+    if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
+    const size_t fixed = (size_t)h.K * 2 + aux + (tw + 15) * 16 * 4;
+    for (int g = 2; g >= 1; --g) {
+      size_t lds = fixed + (size_t)kWaves * g * bufw * 4;
+      if (lds + table > kLdsBytes) continue;
+      if (lds + table < kOneWorkgroupLds) lds = kOneWorkgroupLds - table;
+      if (sub)
+        return g == 2 ? launch_huff_g<2, true>(p, x, y, grid, lds, bufw, st)
+                      : launch_huff_g<1, true>(p, x, y, grid, lds, bufw, st);
+      return g == 2 ? launch_huff_g<2, false>(p, x, y, grid, lds, bufw, st)
+                    : launch_huff_g<1, false>(p, x, y, grid, lds, bufw, st);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, int BITS>
@@ -1713,8 +1788,10 @@ int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* pack
   const hipError_t e = hipMemcpy(&got, packed_dev, sizeof(got), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_status(e);
   if (hptq) {  // the code section's size comes from the stream, so from the blob
+    if (got.hmaxw % 4 || got.hmaxw > (uint32_t)kHuffMaxBlockWords || got.hmaxw > got.hwords) return QGEMV_ERR_SIZE;
+    if (got.hsub > (uint32_t)shape->huff_nsym) return QGEMV_ERR_SIZE;
     expect = make_header(shape->M, shape->K, shape->bits, shape->format, shape->group_size, shape->nnz,
-                         shape->huff_nsym, got.hwords);
+                         shape->huff_nsym, got.hwords, got.hmaxw, got.hsub);
     if (bytes < expect.total_bytes) return QGEMV_ERR_SIZE;
   }
   if (std::memcmp(&got, &expect, sizeof(got)) != 0) return QGEMV_ERR_SIZE;

@@ -52,10 +52,20 @@
 //         HPTQ: per (tile, K-block) the 16 rows' FP16 steps (group 128 = the
 //         K-block).
 // hidx    HPTQ: uint32 [tiles*nkb + 1]; hlane: uint16 [tiles*nkb*64];
-// htab    HPTQ: int32 [4096]: for the next 12 bits of a chunk, (q << 8) | len
-//         of the codeword they start with if len <= 12, else 0; then int32
-//         [3][17]: per length l the first canonical codeword, the number of
-//         codewords and the index of the first in hsym.
+//         the header's hmaxw is the largest block's word count.
+// htab    HPTQ: int32 [4096]: for the next 12 bits of a chunk, the FP16 bits
+//         of the integer of the codeword they start with (bits 16-31) and its
+//         length (bits 0-7) if the length is at most 12; if they start a
+//         longer codeword, 16 times the index of their second-level table
+//         (bits 16-31) and length 0; else 0.  Then int32 [4][17]: per length
+//         l the first canonical codeword, the number of codewords, the index
+//         of the first in hsym, and the end of the codewords of length l
+//         left-justified to 16 bits (the first codeword of length l + 1 would
+//         start there; equal to the previous length's for a length with no
+//         codewords, 0 before the first).  Then int32 [hsub][16]: for each
+//         12-bit prefix of a longer codeword (in prefix order), indexed by
+//         the next 4 bits, FP16 bits of the integer << 16 | length (13-16),
+//         or 16 where no codeword starts.
 // hsym    HPTQ: int16 [hsym]: the codewords' integers in canonical order.
 //         UNIFORM: 512 bytes per (tile, K-block) for its 16 rows x 8 groups of
 //         16 codes: a z plane, FP16 zero points [row][group] (256 B), then an
@@ -78,7 +88,7 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 6;
+constexpr uint32_t kVersion = 8;
 constexpr int kTileRows = 16;
 constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
@@ -105,7 +115,7 @@ struct BlobHeader {
   // tables, codeword integers; number of codewords and of code words.
   uint64_t off_hidx, off_hlane, off_htab, off_hsym;
   int32_t hsym;
-  uint32_t hwords;
+  uint32_t hwords, hmaxw, hsub;
 };
 static_assert(sizeof(BlobHeader) <= kHeaderBytes, "header too large");
 
@@ -113,7 +123,8 @@ inline uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign
 
 // Section offsets of a blob for the given shape.
 inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format, int32_t group,
-                              int64_t nnz, int32_t hsym = 0, uint32_t hwords = 0) {
+                              int64_t nnz, int32_t hsym = 0, uint32_t hwords = 0, uint32_t hmaxw = 0,
+                              uint32_t hsub = 0) {
   const bool hptq = format == 3;
   if (hptq) bits = 0;
   BlobHeader h{};
@@ -139,6 +150,8 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
   h.off_codes = kHeaderBytes;
   h.hsym = hptq ? hsym : 0;
   h.hwords = hptq ? hwords : 0;
+  h.hmaxw = hptq ? hmaxw : 0;
+  h.hsub = hptq ? hsub : 0;
   h.off_meta = align_up(h.off_codes + (hptq ? 4ull * hwords : nblocks * h.block_bytes));
   h.off_rowptr = align_up(h.off_meta + meta_bytes);
   h.off_entries = align_up(h.off_rowptr + 4ull * ((uint64_t)M + 1));
@@ -149,7 +162,7 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
     h.off_hidx = h.total_bytes;
     h.off_hlane = align_up(h.off_hidx + 4ull * (nblocks + 1));
     h.off_htab = align_up(h.off_hlane + 2ull * 64ull * nblocks);
-    h.off_hsym = align_up(h.off_htab + 4ull * (kHuffTable + 3 * 17));
+    h.off_hsym = align_up(h.off_htab + 4ull * (kHuffTable + 4 * 17 + 16ull * hsub));
     h.total_bytes = align_up(h.off_hsym + 2ull * (uint64_t)hsym);
   }
   return h;

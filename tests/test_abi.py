@@ -272,8 +272,11 @@ def _decode_hptq_blob(blob):
     hlane = blob[off_hlane:off_hlane + 2 * 64 * tiles * nkb].view(np.uint16)
     tbits = 12
     nt = 1 << tbits
-    tab = blob[off_htab:off_htab + 4 * (nt + 51)].view(np.int32)
+    tab = blob[off_htab:off_htab + 4 * (nt + 68)].view(np.int32)
     first, count, offs = tab[nt:nt + 17], tab[nt + 17:nt + 34], tab[nt + 34:nt + 51]
+    ljlim = tab[nt + 51:nt + 68]
+    nsub = int(hdr32[39])
+    sub = blob[off_htab + 4 * (nt + 68):off_htab + 4 * (nt + 68 + 16 * nsub)].view(np.int32)
     syms = blob[off_hsym:off_hsym + 2 * nsym].view(np.int16)
     q = np.zeros((tiles * 16, nkb * 128), dtype=np.int64)
     for blk in range(tiles * nkb):
@@ -286,10 +289,19 @@ def _decode_hptq_blob(blob):
             for j in range(32):
                 w0, w1 = int(words[p >> 5]), int(words[(p >> 5) + 1])
                 win = ((w0 << 32 | w1) >> (32 - (p & 31))) & 0xFFFFFFFF
-                e = int(tab[win >> (32 - tbits)])
+                e = int(tab[win >> (32 - tbits)]) & 0xFFFFFFFF
                 if e & 255:
-                    ln, v = e & 255, e >> 8
+                    ln = e & 255
+                    v = np.array([e >> 16], np.uint16).view(np.float16)[0]
+                    assert float(v) == int(v)
+                    v = int(v)
                 else:
+                    # the length is the shortest whose left-justified end lies above the prefix
+                    p16 = win >> 16
+                    ln2 = next(l for l in range(tbits + 1, 17) if p16 < ljlim[l])
+                    # and the second-level table of the 12-bit prefix gives it with its integer
+                    e2 = int(sub[(e >> 16) + (p16 & 15)]) & 0xFFFFFFFF
+                    v2 = int(np.array([e2 >> 16], np.uint16).view(np.float16)[0])
                     for ln in range(tbits + 1, 17):
                         c = win >> (32 - ln)
                         if count[ln] and first[ln] <= c < first[ln] + count[ln]:
@@ -297,6 +309,7 @@ def _decode_hptq_blob(blob):
                             break
                     else:
                         raise AssertionError("no codeword")
+                    assert ln2 == ln and (e2 & 255) == ln and v2 == v
                 q[t * 16 + l % 16, b * 128 + 32 * (l // 16) + j] = v
                 p += ln
     steps = blob[off_meta:off_meta + 32 * tiles * nkb].view(np.uint16).reshape(tiles, nkb, 16)
@@ -333,3 +346,17 @@ def test_hptq_validation():
     blob = qgemv.repack(enc)
     out = np.zeros(4 * 256, np.uint8)
     assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data) == UNS
+
+
+def test_hptq_blob_long_codewords():
+    """The storage-format inputs' code has 14- and 16-bit codewords: the blob's
+    second-level tables and left-justified limits decode them to the integers
+    the stream was written from."""
+    from synth import make_format_inputs
+    f = make_format_inputs("mlp7b_hptq", 0, 37, 1024)
+    f.update(row_ptr=np.zeros(38, np.int32), col_idx=np.zeros(0, np.int32), values=np.zeros(0, np.float16))
+    blob = qgemv.repack(dict(f, fmt="hptq"))
+    assert int(blob[:256].view(np.int32)[39]) > 0  # second-level tables present
+    q, steps = _decode_hptq_blob(blob)
+    assert np.array_equal(q, f["q"])
+    assert np.array_equal(steps, f["scales"].view(np.uint16))
