@@ -465,8 +465,7 @@ static int repack_hptq(const qgemv_weights* w, void* dst_host, size_t bytes) {
   std::memcpy(blob + h.off_hidx, hidx.data(), 4 * hidx.size());
   int32_t* tab = (int32_t*)(blob + h.off_htab);
   int32_t* sub = tab + kHuffTable + 4 * 17;
-  constexpr int kSubBits = kHuffMaxLen - kHuffBits;
-  for (uint32_t i = 0; i < 16u * h.hsub; ++i) sub[i] = kHuffMaxLen;
+  for (uint32_t i = 0; i < (uint32_t)kHuffSub * h.hsub; ++i) sub[i] = kHuffMaxLen;
   int64_t last = -1;
   int nsub = -1;
   for (int k = 0; k < n; ++k) {
@@ -481,10 +480,10 @@ static int repack_hptq(const qgemv_weights* w, void* dst_host, size_t bytes) {
     if ((int64_t)pre != last) {
       ++nsub;
       last = pre;
-      tab[pre] = (int32_t)((uint32_t)(16 * nsub) << 16);
+      tab[pre] = (int32_t)((uint32_t)(kHuffSub * nsub) << 16);
     }
-    const uint32_t lo = (hc.code[k] << (kHuffMaxLen - l)) & ((1u << kSubBits) - 1);
-    for (uint32_t s = 0; s < (1u << (kHuffMaxLen - l)); ++s) sub[16 * nsub + lo + s] = (int32_t)e;
+    const uint32_t lo = (hc.code[k] << (kHuffMaxLen - l)) & (uint32_t)(kHuffSub - 1);
+    for (uint32_t s = 0; s < (1u << (kHuffMaxLen - l)); ++s) sub[kHuffSub * nsub + lo + s] = (int32_t)e;
   }
   int32_t* slow = tab + kHuffTable;
   int32_t lim = 0;

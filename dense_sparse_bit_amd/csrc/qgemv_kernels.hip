@@ -1265,24 +1265,8 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
 // ---------------------------------------------------------------------------
 constexpr int kHuffMaxBlockWords = 64 * kChunkCodes * kHuffMaxLen / 32;  // a block's largest code
 constexpr int kHuffPad = 20;  // words a chain may read past its chunk's start word, and past the block
-constexpr int kHuffMaxSub = 512;  // second-level tables held in LDS (32 KiB)
-
-static_assert(kHuffMaxLen - kHuffBits == 4, "huff_long compares four lengths");
-__device__ __forceinline__ uint32_t huff_long(uint32_t win, uint32_t l0, uint32_t l1, uint32_t l2, int d0, int d1,
-                                              int d2, int d3, const uint16_t* syms, int nsym) {
-  // lengths 13 .. 16: the shortest whose codewords end above the prefix
-  const uint32_t p16 = win >> (32 - kHuffMaxLen);
-  uint32_t len = 16;
-  int d = d3;
-  len = p16 < l2 ? 15u : len;
-  d = p16 < l2 ? d2 : d;
-  len = p16 < l1 ? 14u : len;
-  d = p16 < l1 ? d1 : d;
-  len = p16 < l0 ? 13u : len;
-  d = p16 < l0 ? d0 : d;
-  const uint32_t idx = min((uint32_t)((int)(p16 >> (kHuffMaxLen - len)) + d), (uint32_t)(nsym - 1));
-  return ((uint32_t)syms[idx] << 16) | len;
-}
+constexpr int kHuffMaxSub = 64;  // second-level tables held in LDS (64 KiB)
+constexpr int kHuffLongLens = kHuffMaxLen - kHuffBits;  // lengths a second-level step decodes
 
 template <int G, bool SUB>
 __global__ void __launch_bounds__(64 * kWaves)
@@ -1300,36 +1284,58 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   const int L = TW * nkb;
   const int b0 = w * L / kWaves, b1 = (w + 1) * L / kWaves;  // this wave's run
 
-  // LDS: table [kHuffTable] (static, at address 0) | xs [K] FP16 | aux | slots [TW+15][16]
-  //      | code buffers [16][G][bufw]; aux: the second-level tables [max(nsub, 1)][16]
-  //      (SUB), else the integers [nsym] FP16 (padded)
-  __shared__ int32_t tab[kHuffTable];
+  // LDS: first-level table [kHuffTable][64] (static, at address 0: entry e of
+  //      lane l at e * 64 + l, so that a wave's 64 reads fall in 64 banks)
+  //      | xs [K] FP16 | aux | slots [TW+15][16] | code buffers [16][G][bufw];
+  //      aux: the second-level tables [max(nsub, 1)][kHuffSub] (SUB), else the
+  //      integers [nsym] FP16 (padded)
+  __shared__ uint32_t tab[kHuffTable * 64];
   uint16_t* xs = (uint16_t*)lds;
   uint32_t* aux = lds + K / 2;
   uint16_t* syms = (uint16_t*)aux;
-  const int auxw = SUB ? 16 * max(nsub, 1) : ((nsym + 1) / 2 + 3) / 4 * 4;
+  const int auxw = SUB ? kHuffSub * max(nsub, 1) : ((nsym + 1) / 2 + 3) / 4 * 4;
   float* slots = (float*)(aux + auxw);
   const int bofs = K / 2 + auxw + (TW + 15) * 16 + w * G * bufw;  // in lds, in words
   uint32_t* buf = lds + bofs;
 
   for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
-  for (int i = threadIdx.x; i < kHuffTable / 4; i += 64 * kWaves) ((u32x4_t*)tab)[i] = ((const u32x4_t*)htab)[i];
+  for (int i = threadIdx.x; i < kHuffTable * 16; i += 64 * kWaves) {
+    const uint32_t v = (uint32_t)htab[i >> 4];
+    ((u32x4_t*)tab)[i] = (u32x4_t){v, v, v, v};
+  }
   if (SUB) {
     const u32x4_t* src = (const u32x4_t*)(htab + kHuffTable + 4 * 17);
-    for (int i = threadIdx.x; i < 4 * nsub; i += 64 * kWaves) ((u32x4_t*)aux)[i] = src[i];
+    for (int i = threadIdx.x; i < nsub * (kHuffSub / 4); i += 64 * kWaves) ((u32x4_t*)aux)[i] = src[i];
   } else {
     for (int i = threadIdx.x; i < nsym; i += 64 * kWaves)
       syms[i] = __builtin_bit_cast(uint16_t, (_Float16)(float)hsym[i]);
   }
 
-  // Codewords longer than the table index, lengths 13 .. 16: the
-  // left-justified end of each length's codewords, and the index in syms of
-  // a codeword c of that length minus c.
-  const int32_t* lj = htab + kHuffTable + 51;
-  const int32_t* fi = htab + kHuffTable;
-  const int32_t* of = htab + kHuffTable + 34;
-  const uint32_t l13 = (uint32_t)lj[13], l14 = (uint32_t)lj[14], l15 = (uint32_t)lj[15];
-  const int d13 = of[13] - fi[13], d14 = of[14] - fi[14], d15 = of[15] - fi[15], d16 = of[16] - fi[16];
+  // Codewords longer than the first-level index, lengths kHuffBits+1 .. 16,
+  // without second-level tables: per length the left-justified end of its
+  // codewords, and the index in syms of a codeword c of that length minus c.
+  // The length of a long codeword is the shortest whose end lies above the
+  // prefix.
+  __shared__ int32_t lcl[2 * kHuffLongLens];  // ends, then index offsets
+  if (!SUB && threadIdx.x < kHuffLongLens) {
+    const int l = kHuffBits + 1 + threadIdx.x;
+    lcl[threadIdx.x] = htab[kHuffTable + 51 + l];
+    lcl[kHuffLongLens + threadIdx.x] = htab[kHuffTable + 34 + l] - htab[kHuffTable + l];
+  }
+  auto long_code = [&](uint32_t win) -> uint32_t {
+    const uint32_t p16 = win >> (32 - kHuffMaxLen);
+    uint32_t len = kHuffMaxLen;
+    int d = lcl[2 * kHuffLongLens - 1];
+#pragma unroll
+    for (int k = kHuffLongLens - 2; k >= 0; --k) {
+      const bool in = p16 < (uint32_t)lcl[k];
+      len = in ? (uint32_t)(kHuffBits + 1 + k) : len;
+      d = in ? lcl[kHuffLongLens + k] : d;
+    }
+    const uint32_t idx = min((uint32_t)((int)(p16 >> (kHuffMaxLen - len)) + d), (uint32_t)(nsym - 1));
+    return ((uint32_t)syms[idx] << 16) | len;
+  };
+  const uint32_t lane4 = (uint32_t)lane * 4u;
   const rsrc_t rw = make_rsrc(words, nwords * 4u);
   u32x4_t pre[G];
   uint32_t lbn[G], stn0[G], stn1[G];
@@ -1412,14 +1418,15 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int c = 0; c < G; ++c) e[u][c] = (uint32_t)tab[win[c] >> (32 - kHuffBits)];
+        for (int c = 0; c < G; ++c)
+          e[u][c] = *(const uint32_t*)((const char*)tab + (((win[c] >> (32 - kHuffBits)) << 8) | lane4));
 #pragma unroll
         for (int c = 0; c < G; ++c)
           if ((e[u][c] & 255u) == 0u) {
-            if (SUB)  // the second-level table of these 12 bits, indexed by the next 4
-              e[u][c] = aux[(e[u][c] >> 16) + ((win[c] >> (32 - kHuffMaxLen)) & 15u)];
+            if (SUB)  // the second-level table of these 8 bits, indexed by the next 8
+              e[u][c] = aux[(e[u][c] >> 16) + ((win[c] >> (32 - kHuffMaxLen)) & (uint32_t)(kHuffSub - 1))];
             else
-              e[u][c] = huff_long(win[c], l13, l14, l15, d13, d14, d15, d16, syms, nsym);
+              e[u][c] = long_code(win[c]);
           }
         if (u == 0)
 #pragma unroll
@@ -1709,7 +1716,7 @@ hipError_t launch_huff_g(const qgemv_plan* p, const uint16_t* x, float* y, int g
   const BlobHeader& h = p->h;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)k_huff<G, SUB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)(kLdsBytes - (size_t)kHuffTable * 4));
+                          (int)(kLdsBytes - (size_t)kHuffTable * 64 * 4 - 64));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((k_huff<G, SUB>), dim3(grid), dim3(64 * kWaves), lds, st,
                      (const uint32_t*)(p->blob + h.off_codes), (const uint16_t*)(p->blob + h.off_meta),
@@ -1724,9 +1731,10 @@ hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   const int grid = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
   const int bufw = (int)((h.hmaxw + kHuffPad + 3) / 4 * 4);
-  const size_t table = (size_t)kHuffTable * 4;  // static LDS
+  const size_t table = (size_t)kHuffTable * 64 * 4 + 64;  // static LDS
   for (int sub = 1; sub >= 0; --sub) {
-    const size_t aux = sub ? (size_t)16 * (h.hsub > 1 ? h.hsub : 1) * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
+    const size_t aux =
+        sub ? (size_t)kHuffSub * (h.hsub > 1 ? h.hsub : 1) * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
     if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
     const size_t fixed = (size_t)h.K * 2 + aux + (tw + 15) * 16 * 4;
     for (int g = 2; g >= 1; --g) {

@@ -53,18 +53,18 @@
 //         K-block).
 // hidx    HPTQ: uint32 [tiles*nkb + 1]; hlane: uint16 [tiles*nkb*64];
 //         the header's hmaxw is the largest block's word count.
-// htab    HPTQ: int32 [4096]: for the next 12 bits of a chunk, the FP16 bits
+// htab    HPTQ: int32 [256]: for the next 8 bits of a chunk, the FP16 bits
 //         of the integer of the codeword they start with (bits 16-31) and its
-//         length (bits 0-7) if the length is at most 12; if they start a
-//         longer codeword, 16 times the index of their second-level table
+//         length (bits 0-7) if the length is at most 8; if they start a
+//         longer codeword, 256 times the index of their second-level table
 //         (bits 16-31) and length 0; else 0.  Then int32 [4][17]: per length
 //         l the first canonical codeword, the number of codewords, the index
 //         of the first in hsym, and the end of the codewords of length l
 //         left-justified to 16 bits (the first codeword of length l + 1 would
 //         start there; equal to the previous length's for a length with no
-//         codewords, 0 before the first).  Then int32 [hsub][16]: for each
-//         12-bit prefix of a longer codeword (in prefix order), indexed by
-//         the next 4 bits, FP16 bits of the integer << 16 | length (13-16),
+//         codewords, 0 before the first).  Then int32 [hsub][256]: for each
+//         8-bit prefix of a longer codeword (in prefix order), indexed by
+//         the next 8 bits, FP16 bits of the integer << 16 | length (9-16),
 //         or 16 where no codeword starts.
 // hsym    HPTQ: int16 [hsym]: the codewords' integers in canonical order.
 //         UNIFORM: 512 bytes per (tile, K-block) for its 16 rows x 8 groups of
@@ -88,16 +88,17 @@
 namespace qgemv_layout {
 
 constexpr uint32_t kMagic = 0x564d4751u;  // "QGMV"
-constexpr uint32_t kVersion = 8;
+constexpr uint32_t kVersion = 9;
 constexpr int kTileRows = 16;
 constexpr int kBlockK = 128;
 constexpr int kChunkCodes = 32;
 constexpr int kMaxK = 16384;
 constexpr uint64_t kAlign = 256;
 constexpr uint64_t kHeaderBytes = 256;
-constexpr int kHuffBits = 12;               // HPTQ decode table index: the next 12 bits
+constexpr int kHuffBits = 8;                // HPTQ first-level table index: the next 8 bits
 constexpr int kHuffTable = 1 << kHuffBits;
 constexpr int kHuffMaxLen = 16;
+constexpr int kHuffSub = 1 << (kHuffMaxLen - kHuffBits);  // entries of a second-level table
 constexpr int kHuffMaxSym = 4096;
 
 struct BlobHeader {
@@ -162,7 +163,7 @@ inline BlobHeader make_header(int32_t M, int32_t K, int32_t bits, int32_t format
     h.off_hidx = h.total_bytes;
     h.off_hlane = align_up(h.off_hidx + 4ull * (nblocks + 1));
     h.off_htab = align_up(h.off_hlane + 2ull * 64ull * nblocks);
-    h.off_hsym = align_up(h.off_htab + 4ull * (kHuffTable + 4 * 17 + 16ull * hsub));
+    h.off_hsym = align_up(h.off_htab + 4ull * (kHuffTable + 4 * 17 + (uint64_t)kHuffSub * hsub));
     h.total_bytes = align_up(h.off_hsym + 2ull * (uint64_t)hsym);
   }
   return h;

@@ -270,13 +270,14 @@ def _decode_hptq_blob(blob):
     words = blob[off_codes:off_codes + 4 * int(hidx[-1]) + 8].view(np.uint32)
     words = np.concatenate([words, np.zeros(2, np.uint32)])
     hlane = blob[off_hlane:off_hlane + 2 * 64 * tiles * nkb].view(np.uint16)
-    tbits = 12
+    tbits = 8
     nt = 1 << tbits
     tab = blob[off_htab:off_htab + 4 * (nt + 68)].view(np.int32)
     first, count, offs = tab[nt:nt + 17], tab[nt + 17:nt + 34], tab[nt + 34:nt + 51]
     ljlim = tab[nt + 51:nt + 68]
     nsub = int(hdr32[39])
-    sub = blob[off_htab + 4 * (nt + 68):off_htab + 4 * (nt + 68 + 16 * nsub)].view(np.int32)
+    nsub_e = 1 << (16 - tbits)
+    sub = blob[off_htab + 4 * (nt + 68):off_htab + 4 * (nt + 68 + nsub_e * nsub)].view(np.int32)
     syms = blob[off_hsym:off_hsym + 2 * nsym].view(np.int16)
     q = np.zeros((tiles * 16, nkb * 128), dtype=np.int64)
     for blk in range(tiles * nkb):
@@ -300,7 +301,7 @@ def _decode_hptq_blob(blob):
                     p16 = win >> 16
                     ln2 = next(l for l in range(tbits + 1, 17) if p16 < ljlim[l])
                     # and the second-level table of the 12-bit prefix gives it with its integer
-                    e2 = int(sub[(e >> 16) + (p16 & 15)]) & 0xFFFFFFFF
+                    e2 = int(sub[(e >> 16) + (p16 & (nsub_e - 1))]) & 0xFFFFFFFF
                     v2 = int(np.array([e2 >> 16], np.uint16).view(np.float16)[0])
                     for ln in range(tbits + 1, 17):
                         c = win >> (32 - ln)
