@@ -1247,21 +1247,23 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
 // A (tile, K-block) block holds its 64 lanes' 32-codeword chunks as one bit
 // sequence (qgemv_layout.h).  A wave takes the blocks of its run G at a
 // time: it copies their words into G LDS buffers and decodes the G chunks of
-// each lane side by side, so that the G chains of dependent table reads hide
-// one another's latency.  Each chain keeps the next bits of its chunk in a
-// 64-bit register, refilled from LDS every two codewords (a codeword has at
-// most 16 bits), and looks its top 12 bits up in a 4096-entry table in LDS
-// that gives the FP16 integer and the length of the codeword they start
-// with.  A longer codeword's length is the shortest l whose 16-bit
-// left-justified prefix lies below the end of the canonical codewords of
-// length l (compared without branches against limits held in scalar
-// registers), and its integer one more LDS read.  The integers are exact in
-// FP16 and form the A operand of four MFMAs against x; each row's step
-// scales the block's sums in fp32.  The blocks of a workgroup are cut into
-// 16 runs, one per wave, with a partial slot per (wave, tile) as in k_xlds,
-// and the outputs add the slots in wave order.  The next G blocks' first
-// 1 KiB of code words, lane offsets and steps are loaded while the current
-// ones are decoded.
+// each lane side by side, so that the G chains of dependent LDS reads hide
+// one another's latency.  For each pair of codewords (at most 32 bits) a
+// chain funnel-shifts the two words at its bit position into a 32-bit
+// window.  The window's top 8 bits index the first-level table, which gives
+// the FP16 integer and the length of the codeword they start with; the
+// table is held once per lane (entry e of lane l at e * 64 + l), so that a
+// wave's 64 reads fall in 64 distinct banks.  A longer codeword's 8-bit
+// prefix names a 256-entry second-level table, indexed by the next 8 bits;
+// where those tables do not fit in LDS, the length is the shortest l whose
+// 16-bit left-justified prefix lies below the end of the canonical
+// codewords of length l, and the integer one more read.  The integers are
+// exact in FP16; every 8 codewords of a chunk are the A operand of one MFMA
+// against x, and each row's step scales the block's sums in fp32.  The
+// blocks of a workgroup are cut into 16 runs, one per wave, with a partial
+// slot per (wave, tile) as in k_xlds, and the outputs add the slots in wave
+// order.  The next G blocks' first 1 KiB of code words, lane offsets and
+// steps are loaded while the current ones are decoded.
 // ---------------------------------------------------------------------------
 constexpr int kHuffMaxBlockWords = 64 * kChunkCodes * kHuffMaxLen / 32;  // a block's largest code
 constexpr int kHuffPad = 20;  // words a chain may read past its chunk's start word, and past the block
