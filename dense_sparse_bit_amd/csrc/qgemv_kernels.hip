@@ -1308,6 +1308,10 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   if (SUB) {
     const u32x4_t* src = (const u32x4_t*)(htab + kHuffTable + 4 * 17);
     for (int i = threadIdx.x; i < nsub * (kHuffSub / 4); i += 64 * kWaves) ((u32x4_t*)aux)[i] = src[i];
+    // With no second-level table, bits that start no codeword (a chain with no
+    // block reads stale LDS) still advance by a bounded length.
+    if (nsub == 0)
+      for (int i = threadIdx.x; i < kHuffSub; i += 64 * kWaves) aux[i] = (uint32_t)kHuffMaxLen;
   } else {
     for (int i = threadIdx.x; i < nsym; i += 64 * kWaves)
       syms[i] = __builtin_bit_cast(uint16_t, (_Float16)(float)hsym[i]);

@@ -420,3 +420,79 @@ def test_hptq_full_size_sampled(torch):
     rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.choice(M, size=160, replace=False)]))
     check_y(y, dict(f, fmt="hptq"), x16, rows)
     plan.close()
+
+
+def _hptq_custom(M, K, sym, ln, p_zero, seed):
+    """An HPTQ encoding with a given code: integers drawn from the code's
+    alphabet (0 with probability p_zero), steps U(0.5, 1.5)/64."""
+    from oracle import hptq
+    rng = np.random.default_rng(seed)
+    sym = np.asarray(sym, np.int64)
+    ln = np.asarray(ln, np.int64)
+    s_, l_, codes = hptq.canonical_code(sym, ln)
+    nz = s_[s_ != 0]
+    q = np.where(rng.random((M, K)) < p_zero, 0, rng.choice(nz, size=(M, K)))
+    stream, row_bits = hptq.encode_stream(q, s_, l_, codes)
+    scales = (rng.uniform(0.5, 1.5, size=(M, K // 128)) / 64).astype(np.float16)
+    return {"M": M, "K": K, "fmt": "hptq", "group": 128, "scales": scales, "q": q, "huff_sym": s_.astype(np.int16),
+            "huff_len": l_.astype(np.uint8), "huff_code": codes, "stream": stream, "row_bits": row_bits,
+            "row_ptr": np.zeros(M + 1, np.int32), "col_idx": np.zeros(0, np.int32), "values": np.zeros(0, np.float16)}
+
+
+def _hptq_lds_path(blob, K):
+    """(second-level tables used, blocks decoded side by side) as the launcher chooses them."""
+    h = blob[:256].view(np.int32)
+    nsym, hmaxw, nsub, tiles = int(h[36]), int(h[38]), int(h[39]), int(h[7])
+    tw = -(-tiles // min(tiles, 256))
+    bufw = (hmaxw + 20 + 3) // 4 * 4
+    static = 256 * 64 * 4 + 64
+    for sub in (True, False):
+        if sub and nsub > 64:
+            continue
+        aux = 256 * max(nsub, 1) * 4 if sub else ((nsym + 1) // 2 + 3) // 4 * 4 * 4
+        for g in (2, 1):
+            if static + K * 2 + aux + (tw + 15) * 64 + 16 * g * bufw * 4 <= 160 * 1024:
+                return sub, g
+    return None
+
+
+# 0 -> '0'; 4000 integers +-1..+-2000 of 13 bits: 125 eight-bit prefixes of long codewords
+_CODE13 = ([0] + [v for a in range(1, 2001) for v in (-a, a)], [1] + [13] * 4000)
+# 0 -> '0'; 2048 integers +-1..+-1024 of 16 bits: 8 prefixes
+_CODE16 = ([0] + [v for a in range(1, 1025) for v in (-a, a)], [1] + [16] * 2048)
+
+
+@pytest.mark.parametrize("code,p_zero,M,K,path", [
+    (_CODE13, 0.85, 40, 512, (False, 2)),   # canonical search, two blocks side by side
+    (_CODE13, 0.10, 24, 512, (False, 1)),   # canonical search, large blocks: one at a time
+    (_CODE16, 0.10, 24, 512, (True, 1)),    # second-level tables, large blocks
+])
+def test_hptq_fallback_paths(torch, code, p_zero, M, K, path):
+    from oracle import hptq
+    enc = _hptq_custom(M, K, *code, p_zero, seed=M)
+    blob = qgemv.repack(enc)
+    assert _hptq_lds_path(blob, K) == path
+    _say(f"[gpu] hptq path={path} M={M} K={K} bits/weight={enc['row_bits'][-1] / (M * K):.2f}")
+    x16 = make_x(WORKLOADS["mlp7b_lut3"], 1, K, 0, M)
+    plan = qgemv.QGemv(enc)
+    y1 = run_b1(torch, plan, x16)
+    y_ref, A = hptq.gemv(enc, x16)
+    ok, worst = gemv.within_tolerance(y1, y_ref, A)
+    assert ok, f"tolerance exceeded: worst {worst:.3f}"
+    plan.close()
+
+
+@pytest.mark.parametrize("M,K", [(5, 256), (1, 128)])
+def test_hptq_single_integer(torch, M, K):
+    """An all-zero matrix: one integer, a one-bit code, no second-level table; y is exactly 0."""
+    from oracle import hptq
+    enc = hptq.encode(np.zeros((M, K), np.float16), 128, 3.125)
+    assert len(enc["huff_sym"]) == 1 and int(enc["huff_len"][0]) == 1
+    blob = qgemv.repack(enc)
+    assert int(blob[:256].view(np.int32)[39]) == 0
+    _say(f"[gpu] hptq single integer M={M} K={K}")
+    x16 = make_x(WORKLOADS["mlp7b_lut3"], 1, K, 0, M)
+    plan = qgemv.QGemv(enc)
+    y1 = run_b1(torch, plan, x16)
+    assert np.array_equal(y1, np.zeros_like(y1))
+    plan.close()
