@@ -1270,7 +1270,7 @@ constexpr int kHuffPad = 20;  // words a chain may read past its chunk's start w
 constexpr int kHuffMaxSub = 64;  // second-level tables held in LDS (64 KiB)
 constexpr int kHuffLongLens = kHuffMaxLen - kHuffBits;  // lengths a second-level step decodes
 
-template <int G, bool SUB>
+template <int G, bool SUB, int NB>
 __global__ void __launch_bounds__(64 * kWaves)
 k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, const uint32_t* __restrict__ hidx,
        const uint16_t* __restrict__ hlane, const int32_t* __restrict__ htab, const int16_t* __restrict__ hsym,
@@ -1288,19 +1288,21 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
 
   // LDS: first-level table [kHuffTable][64] (static, at address 0: entry e of
   //      lane l at e * 64 + l, so that a wave's 64 reads fall in 64 banks)
-  //      | xs [K] FP16 | aux | slots [TW+15][16] | code buffers [16][G][bufw];
+  //      | xs [K] FP16 (batch 1) | aux | slots [TW+15][16 rows][NB] | code buffers [16][G][bufw];
   //      aux: the second-level tables [max(nsub, 1)][kHuffSub] (SUB), else the
-  //      integers [nsym] FP16 (padded)
+  //      integers [nsym] FP16 (padded).  At batch 8/16 x stays in L2.
   __shared__ uint32_t tab[kHuffTable * 64];
+  const int xsw = NB == 1 ? K / 2 : 0;
   uint16_t* xs = (uint16_t*)lds;
-  uint32_t* aux = lds + K / 2;
+  uint32_t* aux = lds + xsw;
   uint16_t* syms = (uint16_t*)aux;
   const int auxw = SUB ? kHuffSub * max(nsub, 1) : ((nsym + 1) / 2 + 3) / 4 * 4;
   float* slots = (float*)(aux + auxw);
-  const int bofs = K / 2 + auxw + (TW + 15) * 16 + w * G * bufw;  // in lds, in words
+  const int bofs = xsw + auxw + (TW + 15) * 16 * NB + w * G * bufw;  // in lds, in words
   uint32_t* buf = lds + bofs;
 
-  for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
+  if (NB == 1)
+    for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
   for (int i = threadIdx.x; i < kHuffTable * 16; i += 64 * kWaves) {
     const uint32_t v = (uint32_t)htab[i >> 4];
     ((u32x4_t*)tab)[i] = (u32x4_t){v, v, v, v};
@@ -1343,7 +1345,12 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   };
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const rsrc_t rw = make_rsrc(words, nwords * 4u);
-  u32x4_t pre[G];
+  // batch 8/16: lane l's B operand is batch row l % 16 (zero past NB), columns
+  // 32 (l / 16) + 8i .. +7 of the K-block; rows past NB read out of range
+  const rsrc_t rxb = make_rsrc(x, (uint32_t)(NB * K) * 2u);
+  const int xrow = (lane & 15) < NB ? (lane & 15) * K : -1;
+  constexpr int XP = NB == 1 ? 1 : 4;
+  u32x4_t pre[G], xq[G][XP];
   uint32_t lbn[G], stn0[G], stn1[G];
 #pragma unroll
   for (int c = 0; c < G; ++c) {
@@ -1370,10 +1377,10 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
 
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
   int tl = b0 / nkb;
-  auto flush = [&]() {  // acc[i]: row 4*(lane/16) + i of local tile tl
-    if ((lane & 15) == 0)
+  auto flush = [&]() {  // acc[i]: row 4*(lane/16) + i of local tile tl, batch row lane % 16
+    if ((lane & 15) < NB)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) slots[(w + tl) * 16 + 4 * (lane >> 4) + i] = acc[i];
+      for (int i = 0; i < 4; ++i) slots[((w + tl) * 16 + 4 * (lane >> 4) + i) * NB + (lane & 15)] = acc[i];
   };
   const int sl = 32 * (lane >> 4);
   const uint32_t cap = (uint32_t)(bufw - kHuffPad);
@@ -1396,6 +1403,13 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       }
       st0[c] = stn0[c];
       st1[c] = stn1[c];
+      if (NB > 1) {  // from L2; first used after 8 codewords
+        const int k0 = (bb - (bb / nkb) * nkb) * kBlockK + 32 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < XP; ++i)
+          xq[c][i] = __builtin_amdgcn_raw_buffer_load_b128(
+              rxb, xrow < 0 || bb >= b1 ? (int)kOutOfRange : (xrow + k0 + 8 * i) * 2, 0, 0);
+      }
     }
     prefetch(r0 + G);
 
@@ -1443,8 +1457,13 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
         p[c] += (e[0][c] & 0xffffu) + (e[1][c] & 0xffffu);
         qh[c][(j / 2) & 3] = __builtin_amdgcn_perm(e[1][c], e[0][c], 0x07060302u);
         if ((j & 7) == 6) {
-          const int bb = r0 + c, kb = bb - (bb / nkb) * nkb;
-          const half8_t bx = *(const half8_t*)(xs + kb * kBlockK + sl + j - 6);
+          half8_t bx;
+          if (NB == 1) {
+            const int bb = r0 + c, kb = bb - (bb / nkb) * nkb;
+            bx = *(const half8_t*)(xs + kb * kBlockK + sl + j - 6);
+          } else {
+            bx = __builtin_bit_cast(half8_t, xq[c][NB == 1 ? 0 : (j >> 3)]);
+          }
           blk[c] = mfma(h8(qh[c][0], qh[c][1], qh[c][2], qh[c][3]), bx, blk[c]);
         }
       }
@@ -1469,14 +1488,14 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   }
   if (b0 < b1) flush();
   __syncthreads();
-  for (int r = threadIdx.x; r < nrows; r += 64 * kWaves) {
-    const int t = r >> 4;
+  for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
+    const int r = i / NB, n = i - r * NB, t = r >> 4;
     float v = 0.f;
     for (int u = 0; u < kWaves; ++u) {
       const int c0 = u * L / kWaves, c1 = (u + 1) * L / kWaves;
-      if (c0 < c1 && c0 / nkb <= t && t <= (c1 - 1) / nkb) v += slots[(u + t) * 16 + (r & 15)];
+      if (c0 < c1 && c0 / nkb <= t && t <= (c1 - 1) / nkb) v += slots[((u + t) * 16 + (r & 15)) * NB + n];
     }
-    y[T0 * 16 + r] = v;
+    y[(size_t)n * M + T0 * 16 + r] = v;
   }
 }
 
@@ -1712,19 +1731,19 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   return hipGetLastError();
 }
 
-// HPTQ, batch 1: one workgroup per CU over its tile range; G = 2 blocks
-// decoded side by side per wave where their buffers fit in LDS, else one.
-// Long codewords go through the second-level tables where they fit in LDS,
-// else through the canonical search.
-template <int G, bool SUB>
+// HPTQ: one workgroup per CU over its tile range; G = 2 blocks decoded side
+// by side per wave where their buffers fit in LDS, else one.  Long codewords
+// go through the second-level tables where they fit in LDS, else through the
+// canonical search.  x sits in LDS at batch 1 and is read from L2 at 8/16.
+template <int G, bool SUB, int NB>
 hipError_t launch_huff_g(const qgemv_plan* p, const uint16_t* x, float* y, int grid, size_t lds, int bufw,
                          hipStream_t st) {
   const BlobHeader& h = p->h;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_huff<G, SUB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      hipFuncSetAttribute((const void*)k_huff<G, SUB, NB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)(kLdsBytes - (size_t)kHuffTable * 64 * 4 - 64));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_huff<G, SUB>), dim3(grid), dim3(64 * kWaves), lds, st,
+  hipLaunchKernelGGL((k_huff<G, SUB, NB>), dim3(grid), dim3(64 * kWaves), lds, st,
                      (const uint32_t*)(p->blob + h.off_codes), (const uint16_t*)(p->blob + h.off_meta),
                      (const uint32_t*)(p->blob + h.off_hidx), (const uint16_t*)(p->blob + h.off_hlane),
                      (const int32_t*)(p->blob + h.off_htab), (const int16_t*)(p->blob + h.off_hsym), x, y, h.M, h.K,
@@ -1732,7 +1751,8 @@ hipError_t launch_huff_g(const qgemv_plan* p, const uint16_t* x, float* y, int g
   return hipGetLastError();
 }
 
-hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+template <int NB>
+hipError_t launch_huff_nb(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
   const BlobHeader& h = p->h;
   const int grid = h.tiles < kMaxGrid ? h.tiles : kMaxGrid;
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
@@ -1742,19 +1762,25 @@ hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
     const size_t aux =
         sub ? (size_t)kHuffSub * (h.hsub > 1 ? h.hsub : 1) * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
     if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
-    const size_t fixed = (size_t)h.K * 2 + aux + (tw + 15) * 16 * 4;
+    const size_t fixed = (NB == 1 ? (size_t)h.K * 2 : 0) + aux + (tw + 15) * 16 * NB * 4;
     for (int g = 2; g >= 1; --g) {
       size_t lds = fixed + (size_t)kWaves * g * bufw * 4;
       if (lds + table > kLdsBytes) continue;
       if (lds + table < kOneWorkgroupLds) lds = kOneWorkgroupLds - table;
       if (sub)
-        return g == 2 ? launch_huff_g<2, true>(p, x, y, grid, lds, bufw, st)
-                      : launch_huff_g<1, true>(p, x, y, grid, lds, bufw, st);
-      return g == 2 ? launch_huff_g<2, false>(p, x, y, grid, lds, bufw, st)
-                    : launch_huff_g<1, false>(p, x, y, grid, lds, bufw, st);
+        return g == 2 ? launch_huff_g<2, true, NB>(p, x, y, grid, lds, bufw, st)
+                      : launch_huff_g<1, true, NB>(p, x, y, grid, lds, bufw, st);
+      return g == 2 ? launch_huff_g<2, false, NB>(p, x, y, grid, lds, bufw, st)
+                    : launch_huff_g<1, false, NB>(p, x, y, grid, lds, bufw, st);
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, int batch, hipStream_t st) {
+  return batch == 1   ? launch_huff_nb<1>(p, x, y, st)
+         : batch == 8 ? launch_huff_nb<8>(p, x, y, st)
+                      : launch_huff_nb<16>(p, x, y, st);
 }
 
 template <int FMT, int BITS>
@@ -1823,10 +1849,7 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
   const uint16_t* x = (const uint16_t*)x_dev;
   const bool b4 = h->h.bits == 4;
   hipError_t e;
-  if (h->h.format == QGEMV_FMT_HPTQ) {
-    if (batch != 1) return QGEMV_ERR_UNSUPPORTED;
-    return hip_status(launch_huff(h, x, y_dev, st));
-  }
+  if (h->h.format == QGEMV_FMT_HPTQ) return hip_status(launch_huff(h, x, y_dev, batch, st));
   if (h->h.format == QGEMV_FMT_LUT)
     e = b4 ? launch_run<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_run<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
   else if (h->h.format == QGEMV_FMT_BPDQ)

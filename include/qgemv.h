@@ -103,7 +103,7 @@ typedef enum {
  *               is all zeros).
  *   row_bits    int64 [M+1]: row_bits[0] = 0, row i holds exactly K codewords
  *               in bits [row_bits[i], row_bits[i+1]).
- * An HPTQ plan runs at batch 1 only (UNSUPPORTED otherwise).
+ * An HPTQ plan runs at every batch (1, 8, 16); the decode is the same.
  *   row_ptr     int32 [M+1]: row_ptr[0] = 0, non-decreasing, row_ptr[M] = nnz.
  *   col_idx     int32 [nnz]: 0 <= c < K, strictly ascending inside a row.
  *   values      FP16 bits [nnz], finite.  col_idx/values may be NULL iff nnz == 0.

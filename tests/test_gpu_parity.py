@@ -401,10 +401,15 @@ def test_hptq_oracle_encoded(torch, M, K, bpw):
     assert ok, f"tolerance exceeded: worst {worst:.3f}"
     y2 = run_b1(torch, plan, x16)
     assert np.array_equal(y1, y2), "not bitwise deterministic"
-    xb = torch.zeros((8, K), dtype=torch.float16, device="cuda")
-    yb = torch.zeros((8, M), dtype=torch.float32, device="cuda")
-    s = torch.cuda.current_stream().cuda_stream
-    assert qgemv.lib().qgemv_run(plan._h, xb.data_ptr(), yb.data_ptr(), 8, s) == -3
+    for B in (8, 16):  # x from L2, one MFMA column per batch row
+        xb = make_x(wl, B, K, 0, M)
+        yb = run_bn(torch, plan, xb)
+        yr, Ab = hptq.gemv(enc, xb)
+        ok, worst = gemv.within_tolerance(yb, yr, Ab)
+        assert ok, f"batch {B}: tolerance exceeded: worst {worst:.3f}"
+        assert np.array_equal(yb, run_bn(torch, plan, xb)), "batched run not bitwise deterministic"
+        y1b = run_b1(torch, plan, xb[B - 1:B])
+        assert np.all(np.abs(yb[B - 1] - y1b[0]) <= 2e-4 * Ab[B - 1] + 2e-6)
     plan.close()
 
 
@@ -419,6 +424,9 @@ def test_hptq_full_size_sampled(torch):
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.choice(M, size=160, replace=False)]))
     check_y(y, dict(f, fmt="hptq"), x16, rows)
+    xb = make_x("mlp7b_hptq", 16, K, 0, M)
+    yb = run_bn(torch, plan, xb)
+    check_y(yb, dict(f, fmt="hptq"), xb, rows)
     plan.close()
 
 
@@ -479,6 +487,11 @@ def test_hptq_fallback_paths(torch, code, p_zero, M, K, path):
     y_ref, A = hptq.gemv(enc, x16)
     ok, worst = gemv.within_tolerance(y1, y_ref, A)
     assert ok, f"tolerance exceeded: worst {worst:.3f}"
+    xb = make_x(WORKLOADS["mlp7b_lut3"], 8, K, 0, M)
+    yb = run_bn(torch, plan, xb)
+    yr, Ab = hptq.gemv(enc, xb)
+    ok, worst = gemv.within_tolerance(yb, yr, Ab)
+    assert ok, f"batch 8: tolerance exceeded: worst {worst:.3f}"
     plan.close()
 
 
