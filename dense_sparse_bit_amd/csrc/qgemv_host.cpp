@@ -225,7 +225,10 @@ struct HuffCode {
   int first[kHuffMaxLen + 1], count[kHuffMaxLen + 1], offset[kHuffMaxLen + 1];
 };
 
-// Number of distinct kHuffBits-bit prefixes among codewords longer than kHuffBits.
+// Number of second-level tables: the distinct kHuffBits-bit prefixes among
+// codewords longer than kHuffBits, at least 1 (with no long codeword, one
+// table of length-16 entries keeps a decoder that meets bits starting no
+// codeword advancing by a bounded length).
 static uint32_t hptq_nsub(const qgemv_weights* w, const HuffCode& hc) {
   uint32_t n = 0;
   int64_t last = -1;
@@ -236,7 +239,7 @@ static uint32_t hptq_nsub(const qgemv_weights* w, const HuffCode& hc) {
     if (pre != last) ++n;
     last = pre;
   }
-  return n;
+  return n > 0 ? n : 1;
 }
 
 static int hptq_code(const qgemv_weights* w, HuffCode& hc) {

@@ -1289,19 +1289,19 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   // LDS: first-level table [kHuffTable][64] (static, at address 0: entry e of
   //      lane l at e * 64 + l, so that a wave's 64 reads fall in 64 banks)
   //      | xs [K] FP16 (batch 1) | aux | slots [TW+15][16 rows][NB] | code buffers [16][G][bufw];
-  //      aux: the second-level tables [max(nsub, 1)][kHuffSub] (SUB), else the
+  //      aux: the second-level tables [nsub][kHuffSub] (SUB), else the
   //      integers [nsym] FP16 (padded).  At batch 8/16 x stays in L2.
   __shared__ uint32_t tab[kHuffTable * 64];
   const int xsw = NB == 1 ? K / 2 : 0;
   uint16_t* xs = (uint16_t*)lds;
   uint32_t* aux = lds + xsw;
   uint16_t* syms = (uint16_t*)aux;
-  const int auxw = SUB ? kHuffSub * max(nsub, 1) : ((nsym + 1) / 2 + 3) / 4 * 4;
+  const int auxw = SUB ? kHuffSub * nsub : ((nsym + 1) / 2 + 3) / 4 * 4;
   float* slots = (float*)(aux + auxw);
   const int bofs = xsw + auxw + (TW + 15) * 16 * NB + w * G * bufw;  // in lds, in words
   uint32_t* buf = lds + bofs;
 
-  if (NB == 1)
+  if constexpr (NB == 1)
     for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
   for (int i = threadIdx.x; i < kHuffTable * 16; i += 64 * kWaves) {
     const uint32_t v = (uint32_t)htab[i >> 4];
@@ -1310,10 +1310,6 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   if (SUB) {
     const u32x4_t* src = (const u32x4_t*)(htab + kHuffTable + 4 * 17);
     for (int i = threadIdx.x; i < nsub * (kHuffSub / 4); i += 64 * kWaves) ((u32x4_t*)aux)[i] = src[i];
-    // With no second-level table, bits that start no codeword (a chain with no
-    // block reads stale LDS) still advance by a bounded length.
-    if (nsub == 0)
-      for (int i = threadIdx.x; i < kHuffSub; i += 64 * kWaves) aux[i] = (uint32_t)kHuffMaxLen;
   } else {
     for (int i = threadIdx.x; i < nsym; i += 64 * kWaves)
       syms[i] = __builtin_bit_cast(uint16_t, (_Float16)(float)hsym[i]);
@@ -1347,8 +1343,8 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   const rsrc_t rw = make_rsrc(words, nwords * 4u);
   // batch 8/16: lane l's B operand is batch row l % 16 (zero past NB), columns
   // 32 (l / 16) + 8i .. +7 of the K-block; rows past NB read out of range
-  const rsrc_t rxb = make_rsrc(x, (uint32_t)(NB * K) * 2u);
-  const int xrow = (lane & 15) < NB ? (lane & 15) * K : -1;
+  const rsrc_t rxb = make_rsrc(x, NB == 1 ? 0u : (uint32_t)(NB * K) * 2u);
+  const int xrow = NB > 1 && (lane & 15) < NB ? (lane & 15) * K : -1;
   constexpr int XP = NB == 1 ? 1 : 4;
   u32x4_t pre[G], xq[G][XP];
   uint32_t lbn[G], stn0[G], stn1[G];
@@ -1378,9 +1374,15 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
   int tl = b0 / nkb;
   auto flush = [&]() {  // acc[i]: row 4*(lane/16) + i of local tile tl, batch row lane % 16
-    if ((lane & 15) < NB)
+    if constexpr (NB == 1) {
+      if ((lane & 15) == 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) slots[((w + tl) * 16 + 4 * (lane >> 4) + i) * NB + (lane & 15)] = acc[i];
+        for (int i = 0; i < 4; ++i) slots[(w + tl) * 16 + 4 * (lane >> 4) + i] = acc[i];
+    } else {
+      if ((lane & 15) < NB)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slots[((w + tl) * 16 + 4 * (lane >> 4) + i) * NB + (lane & 15)] = acc[i];
+    }
   };
   const int sl = 32 * (lane >> 4);
   const uint32_t cap = (uint32_t)(bufw - kHuffPad);
@@ -1403,7 +1405,7 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       }
       st0[c] = stn0[c];
       st1[c] = stn1[c];
-      if (NB > 1) {  // from L2; first used after 8 codewords
+      if constexpr (NB > 1) {  // from L2; first used after 8 codewords
         const int k0 = (bb - (bb / nkb) * nkb) * kBlockK + 32 * (lane >> 4);
 #pragma unroll
         for (int i = 0; i < XP; ++i)
@@ -1458,7 +1460,7 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
         qh[c][(j / 2) & 3] = __builtin_amdgcn_perm(e[1][c], e[0][c], 0x07060302u);
         if ((j & 7) == 6) {
           half8_t bx;
-          if (NB == 1) {
+          if constexpr (NB == 1) {
             const int bb = r0 + c, kb = bb - (bb / nkb) * nkb;
             bx = *(const half8_t*)(xs + kb * kBlockK + sl + j - 6);
           } else {
@@ -1489,13 +1491,13 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   if (b0 < b1) flush();
   __syncthreads();
   for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
-    const int r = i / NB, n = i - r * NB, t = r >> 4;
+    const int r = NB == 1 ? i : i / NB, n = NB == 1 ? 0 : i - r * NB, t = r >> 4;
     float v = 0.f;
     for (int u = 0; u < kWaves; ++u) {
       const int c0 = u * L / kWaves, c1 = (u + 1) * L / kWaves;
       if (c0 < c1 && c0 / nkb <= t && t <= (c1 - 1) / nkb) v += slots[((u + t) * 16 + (r & 15)) * NB + n];
     }
-    y[(size_t)n * M + T0 * 16 + r] = v;
+    y[n * M + T0 * 16 + r] = v;
   }
 }
 
@@ -1760,7 +1762,7 @@ hipError_t launch_huff_nb(const qgemv_plan* p, const uint16_t* x, float* y, hipS
   const size_t table = (size_t)kHuffTable * 64 * 4 + 64;  // static LDS
   for (int sub = 1; sub >= 0; --sub) {
     const size_t aux =
-        sub ? (size_t)kHuffSub * (h.hsub > 1 ? h.hsub : 1) * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
+        sub ? (size_t)kHuffSub * h.hsub * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
     if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
     const size_t fixed = (NB == 1 ? (size_t)h.K * 2 : 0) + aux + (tw + 15) * 16 * NB * 4;
     for (int g = 2; g >= 1; --g) {
@@ -1829,7 +1831,7 @@ int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* pack
   if (e != hipSuccess) return hip_status(e);
   if (hptq) {  // the code section's size comes from the stream, so from the blob
     if (got.hmaxw % 4 || got.hmaxw > (uint32_t)kHuffMaxBlockWords || got.hmaxw > got.hwords) return QGEMV_ERR_SIZE;
-    if (got.hsub > (uint32_t)shape->huff_nsym) return QGEMV_ERR_SIZE;
+    if (got.hsub < 1 || got.hsub > (uint32_t)shape->huff_nsym) return QGEMV_ERR_SIZE;
     expect = make_header(shape->M, shape->K, shape->bits, shape->format, shape->group_size, shape->nnz,
                          shape->huff_nsym, got.hwords, got.hmaxw, got.hsub);
     if (bytes < expect.total_bytes) return QGEMV_ERR_SIZE;

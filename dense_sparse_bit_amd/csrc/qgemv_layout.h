@@ -65,7 +65,8 @@
 //         codewords, 0 before the first).  Then int32 [hsub][256]: for each
 //         8-bit prefix of a longer codeword (in prefix order), indexed by
 //         the next 8 bits, FP16 bits of the integer << 16 | length (9-16),
-//         or 16 where no codeword starts.
+//         or 16 where no codeword starts; at least one table (with no longer
+//         codeword, one of length-16 entries).
 // hsym    HPTQ: int16 [hsym]: the codewords' integers in canonical order.
 //         UNIFORM: 512 bytes per (tile, K-block) for its 16 rows x 8 groups of
 //         16 codes: a z plane, FP16 zero points [row][group] (256 B), then an

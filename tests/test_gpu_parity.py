@@ -497,12 +497,12 @@ def test_hptq_fallback_paths(torch, code, p_zero, M, K, path):
 
 @pytest.mark.parametrize("M,K", [(5, 256), (1, 128)])
 def test_hptq_single_integer(torch, M, K):
-    """An all-zero matrix: one integer, a one-bit code, no second-level table; y is exactly 0."""
+    """An all-zero matrix: one integer, a one-bit code, only the filler second-level table; y is exactly 0."""
     from oracle import hptq
     enc = hptq.encode(np.zeros((M, K), np.float16), 128, 3.125)
     assert len(enc["huff_sym"]) == 1 and int(enc["huff_len"][0]) == 1
     blob = qgemv.repack(enc)
-    assert int(blob[:256].view(np.int32)[39]) == 0
+    assert int(blob[:256].view(np.int32)[39]) == 1
     _say(f"[gpu] hptq single integer M={M} K={K}")
     x16 = make_x(WORKLOADS["mlp7b_lut3"], 1, K, 0, M)
     plan = qgemv.QGemv(enc)
