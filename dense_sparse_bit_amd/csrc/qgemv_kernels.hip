@@ -1269,6 +1269,7 @@ constexpr int kHuffMaxBlockWords = 64 * kChunkCodes * kHuffMaxLen / 32;  // a bl
 constexpr int kHuffPad = 20;  // words a chain may read past its chunk's start word, and past the block
 constexpr int kHuffMaxSub = 64;  // second-level tables held in LDS (64 KiB)
 constexpr int kHuffLongLens = kHuffMaxLen - kHuffBits;  // lengths a second-level step decodes
+static_assert(kHuffBits == 8, "the first-level address takes the window's top byte");
 
 template <int G, bool SUB, int NB>
 __global__ void __launch_bounds__(64 * kWaves)
@@ -1434,14 +1435,14 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       uint32_t win[G], e[2][G];
 #pragma unroll
       for (int c = 0; c < G; ++c) {
-        const uint32_t k = (uint32_t)(bofs + c * bufw - 1) + (p[c] >> 5);
+        const uint32_t k = (uint32_t)(bofs + c * bufw - 1) + __builtin_amdgcn_ubfe(p[c], 5, 27);
         win[c] = __builtin_amdgcn_alignbit(lds[k], lds[k + 1], ~p[c]);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int c = 0; c < G; ++c)
-          e[u][c] = *(const uint32_t*)((const char*)tab + (((win[c] >> (32 - kHuffBits)) << 8) | lane4));
+        for (int c = 0; c < G; ++c)  // byte address: lane * 4 | top window byte << 8
+          e[u][c] = *(const uint32_t*)((const char*)tab + perm(win[c], lane4, 0x0C0C0700u));
 #pragma unroll
         for (int c = 0; c < G; ++c)
           if ((e[u][c] & 255u) == 0u) {
@@ -1456,7 +1457,8 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       }
 #pragma unroll
       for (int c = 0; c < G; ++c) {
-        p[c] += (e[0][c] & 0xffffu) + (e[1][c] & 0xffffu);
+        p[c] += e[0][c] & 0xffffu;
+        p[c] += e[1][c] & 0xffffu;
         qh[c][(j / 2) & 3] = __builtin_amdgcn_perm(e[1][c], e[0][c], 0x07060302u);
         if ((j & 7) == 6) {
           half8_t bx;
