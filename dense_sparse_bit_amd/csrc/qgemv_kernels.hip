@@ -1270,6 +1270,9 @@ constexpr int kHuffPad = 20;  // words a chain may read past its chunk's start w
 constexpr int kHuffMaxSub = 64;  // second-level tables held in LDS (64 KiB)
 constexpr int kHuffLongLens = kHuffMaxLen - kHuffBits;  // lengths a second-level step decodes
 static_assert(kHuffBits == 8, "the first-level address takes the window's top byte");
+static_assert(kWaves == 16 && kHuffTable * 16 == 4 * 1024 && kMaxK / 8 <= 2 * 1024 &&
+                  kHuffMaxSub * kHuffSub / 4 <= 4 * 1024,
+              "the prologue stages x, the tables and the second-level tables in fixed rounds of 1024 threads");
 
 template <int G, bool SUB, int NB>
 __global__ void __launch_bounds__(64 * kWaves)
@@ -1291,7 +1294,8 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   //      lane l at e * 64 + l, so that a wave's 64 reads fall in 64 banks)
   //      | xs [K] FP16 (batch 1) | aux | slots [TW+15][16 rows][NB] | code buffers [16][G][bufw];
   //      aux: the second-level tables [nsub][kHuffSub] (SUB), else the
-  //      integers [nsym] FP16 (padded).  At batch 8/16 x stays in L2.
+  //      integers [nsym] FP16 (padded).  At batch 8/16 x stays in L2.  Then
+  //      the workgroup's block word offsets hidx[T0 * nkb .. T1 * nkb] (padded).
   __shared__ uint32_t tab[kHuffTable * 64];
   const int xsw = NB == 1 ? K / 2 : 0;
   uint16_t* xs = (uint16_t*)lds;
@@ -1299,22 +1303,38 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   uint16_t* syms = (uint16_t*)aux;
   const int auxw = SUB ? kHuffSub * nsub : ((nsym + 1) / 2 + 3) / 4 * 4;
   float* slots = (float*)(aux + auxw);
-  const int bofs = xsw + auxw + (TW + 15) * 16 * NB + w * G * bufw;  // in lds, in words
+  uint32_t* hl = (uint32_t*)(slots + (TW + 15) * 16 * NB);
+  const int bofs = xsw + auxw + (TW + 15) * 16 * NB + ((L + 4) & ~3) + w * G * bufw;  // in lds, in words
   uint32_t* buf = lds + bofs;
 
-  if constexpr (NB == 1)
-    for (int i = threadIdx.x; i < K / 8; i += 64 * kWaves) ((u32x4_t*)xs)[i] = ((const u32x4_t*)x)[i];
-  for (int i = threadIdx.x; i < kHuffTable * 16; i += 64 * kWaves) {
-    const uint32_t v = (uint32_t)htab[i >> 4];
-    ((u32x4_t*)tab)[i] = (u32x4_t){v, v, v, v};
-  }
-  if (SUB) {
-    const u32x4_t* src = (const u32x4_t*)(htab + kHuffTable + 4 * 17);
-    for (int i = threadIdx.x; i < nsub * (kHuffSub / 4); i += 64 * kWaves) ((u32x4_t*)aux)[i] = src[i];
-  } else {
-    for (int i = threadIdx.x; i < nsym; i += 64 * kWaves)
-      syms[i] = __builtin_bit_cast(uint16_t, (_Float16)(float)hsym[i]);
-  }
+  // Prologue: every load first, then the LDS stores, so the latencies overlap.
+  // x: pieces tid, tid + 1024 (K <= 16384); first-level entries (i >> 4) for
+  // pieces i = tid + 1024 k, k < 4; second-level pieces tid + 1024 k (nsub <= 64).
+  const int tid = (int)threadIdx.x;
+  u32x4_t xv[2], av[4];
+  uint32_t tv[4];
+  const u32x4_t* asrc = (const u32x4_t*)(htab + kHuffTable + 4 * 17);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (NB == 1 && tid + 1024 * k < K / 8) xv[k] = ((const u32x4_t*)x)[tid + 1024 * k];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tv[k] = (uint32_t)htab[(tid + 1024 * k) >> 4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (SUB && tid + 1024 * k < nsub * (kHuffSub / 4)) av[k] = asrc[tid + 1024 * k];
+  const uint32_t hv = tid <= L ? hidx[T0 * nkb + tid] : 0u;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (NB == 1 && tid + 1024 * k < K / 8) ((u32x4_t*)xs)[tid + 1024 * k] = xv[k];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ((u32x4_t*)tab)[tid + 1024 * k] = (u32x4_t){tv[k], tv[k], tv[k], tv[k]};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (SUB && tid + 1024 * k < nsub * (kHuffSub / 4)) ((u32x4_t*)aux)[tid + 1024 * k] = av[k];
+  if (tid <= L) hl[tid] = hv;
+  for (int i = tid + 1024; i <= L; i += 64 * kWaves) hl[i] = hidx[T0 * nkb + i];  // runs past 1024 blocks
+  if (!SUB)
+    for (int i = tid; i < nsym; i += 64 * kWaves) syms[i] = __builtin_bit_cast(uint16_t, (_Float16)(float)hsym[i]);
 
   // Codewords longer than the first-level index, lengths kHuffBits+1 .. 16,
   // without second-level tables: per length the left-justified end of its
@@ -1354,13 +1374,15 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
     pre[c] = (u32x4_t){0u, 0u, 0u, 0u};
     lbn[c] = stn0[c] = stn1[c] = 0u;
   }
-  auto prefetch = [&](int r0) {  // per block: first 1 KiB of words, lane offset, steps of rows 4*(lane/16) .. +3
+  // per block: first 1 KiB of words, lane offset, steps of rows 4*(lane/16) .. +3;
+  // the block offsets come from LDS once the prologue's barrier has passed
+  auto prefetch = [&](int r0, bool first) {
 #pragma unroll
     for (int c = 0; c < G; ++c) {
       const int bb = r0 + c;
       if (bb < b1) {
         const int g = T0 * nkb + bb;
-        const uint32_t wo = hidx[g];
+        const uint32_t wo = first ? hidx[g] : __builtin_amdgcn_readfirstlane(hl[bb]);
         pre[c] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((wo + 4u * (uint32_t)lane) * 4u), 0, kNonTemporal);
         lbn[c] = hlane[(size_t)g * 64 + lane];
         const uint32_t* sp = (const uint32_t*)(steps + (size_t)g * 16 + 4 * (lane >> 4));
@@ -1369,7 +1391,7 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       }
     }
   };
-  prefetch(b0);
+  prefetch(b0, true);
   __syncthreads();
 
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -1396,8 +1418,8 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       lb[c] = 0u;
       if (bb < b1) {
         const int t = bb / nkb;
-        const int g = T0 * nkb + bb;
-        const uint32_t wo = hidx[g], nw = min(hidx[g + 1] - wo, cap);  // a multiple of 4
+        const uint32_t wo = __builtin_amdgcn_readfirstlane(hl[bb]);
+        const uint32_t nw = min(__builtin_amdgcn_readfirstlane(hl[bb + 1]) - wo, cap);  // a multiple of 4
         // the block's words: the first 1 KiB from the prefetch, any more now
         if (4 * lane < (int)nw) ((u32x4_t*)bc)[lane] = pre[c];
         for (uint32_t i = 256u + 4u * (uint32_t)lane; i < nw; i += 256u)
@@ -1414,29 +1436,30 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
               rxb, xrow < 0 || bb >= b1 ? (int)kOutOfRange : (xrow + k0 + 8 * i) * 2, 0, 0);
       }
     }
-    prefetch(r0 + G);
+    prefetch(r0 + G, false);
 
     // decode the G chunks of this lane, 32 codewords each, side by side; every
     // 8 codewords of a chunk are one MFMA A operand.  Each pair of codewords
     // (at most 32 bits) is the 32-bit window at the chunk's bit position: with
     // p = position + 31, the words p/32 - 1 and p/32 funnel-shifted right by
-    // -position mod 32.  Rows past M decode whatever their lanes read; their
-    // sums are never stored.
+    // -position mod 32.  A chain keeps np = ~p: the shift is np mod 32, and
+    // p/32 = ~(np >> 5) with an arithmetic shift.  Rows past M decode whatever
+    // their lanes read; their sums are never stored.
     uint32_t qh[G][4];
     floatx4_t blk[G];
-    uint32_t p[G];
+    uint32_t np[G];
 #pragma unroll
     for (int c = 0; c < G; ++c) {
       blk[c] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-      p[c] = lb[c] + 31u;
+      np[c] = ~(lb[c] + 31u);
     }
 #pragma unroll
     for (int j = 0; j < 32; j += 2) {
       uint32_t win[G], e[2][G];
 #pragma unroll
       for (int c = 0; c < G; ++c) {
-        const uint32_t k = (uint32_t)(bofs + c * bufw - 1) + __builtin_amdgcn_ubfe(p[c], 5, 27);
-        win[c] = __builtin_amdgcn_alignbit(lds[k], lds[k + 1], ~p[c]);
+        const int k = (bofs + c * bufw - 2) - ((int)np[c] >> 5);
+        win[c] = __builtin_amdgcn_alignbit(lds[k], lds[k + 1], np[c]);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -1457,8 +1480,8 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       }
 #pragma unroll
       for (int c = 0; c < G; ++c) {
-        p[c] += e[0][c] & 0xffffu;
-        p[c] += e[1][c] & 0xffffu;
+        np[c] -= e[0][c] & 0xffffu;
+        np[c] -= e[1][c] & 0xffffu;
         qh[c][(j / 2) & 3] = __builtin_amdgcn_perm(e[1][c], e[0][c], 0x07060302u);
         if ((j & 7) == 6) {
           half8_t bx;
@@ -1766,7 +1789,8 @@ hipError_t launch_huff_nb(const qgemv_plan* p, const uint16_t* x, float* y, hipS
     const size_t aux =
         sub ? (size_t)kHuffSub * h.hsub * 4 : (size_t)(((h.hsym + 1) / 2 + 3) / 4 * 4) * 4;
     if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
-    const size_t fixed = (NB == 1 ? (size_t)h.K * 2 : 0) + aux + (tw + 15) * 16 * NB * 4;
+    const size_t fixed = (NB == 1 ? (size_t)h.K * 2 : 0) + aux + (tw + 15) * 16 * NB * 4 +
+                         ((tw * (size_t)h.nkb + 4) & ~(size_t)3) * 4;
     for (int g = 2; g >= 1; --g) {
       size_t lds = fixed + (size_t)kWaves * g * bufw * 4;
       if (lds + table > kLdsBytes) continue;
