@@ -1758,8 +1758,9 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   return hipGetLastError();
 }
 
-// HPTQ: one workgroup per CU over its tile range; G = 2 blocks decoded side
-// by side per wave where their buffers fit in LDS, else one.  Long codewords
+// HPTQ: one workgroup per CU over its tile range; G = 3 blocks decoded side
+// by side per wave (2 at batch 8/16) where their buffers fit in LDS, else
+// fewer.  Long codewords
 // go through the second-level tables where they fit in LDS, else through the
 // canonical search.  x sits in LDS at batch 1 and is read from L2 at 8/16.
 template <int G, bool SUB, int NB>
@@ -1791,10 +1792,14 @@ hipError_t launch_huff_nb(const qgemv_plan* p, const uint16_t* x, float* y, hipS
     if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
     const size_t fixed = (NB == 1 ? (size_t)h.K * 2 : 0) + aux + (tw + 15) * 16 * NB * 4 +
                          ((tw * (size_t)h.nkb + 4) & ~(size_t)3) * 4;
-    for (int g = 2; g >= 1; --g) {
+    for (int g = NB == 1 ? 3 : 2; g >= 1; --g) {  // three chains' x pieces would spill at batch 8/16
       size_t lds = fixed + (size_t)kWaves * g * bufw * 4;
       if (lds + table > kLdsBytes) continue;
       if (lds + table < kOneWorkgroupLds) lds = kOneWorkgroupLds - table;
+      if constexpr (NB == 1)
+        if (g == 3)
+          return sub ? launch_huff_g<3, true, NB>(p, x, y, grid, lds, bufw, st)
+                     : launch_huff_g<3, false, NB>(p, x, y, grid, lds, bufw, st);
       if (sub)
         return g == 2 ? launch_huff_g<2, true, NB>(p, x, y, grid, lds, bufw, st)
                       : launch_huff_g<1, true, NB>(p, x, y, grid, lds, bufw, st);

@@ -448,18 +448,19 @@ def _hptq_custom(M, K, sym, ln, p_zero, seed):
 
 
 def _hptq_lds_path(blob, K):
-    """(second-level tables used, blocks decoded side by side) as the launcher chooses them."""
+    """(second-level tables used, blocks decoded side by side) as the launcher chooses them at batch 1."""
     h = blob[:256].view(np.int32)
-    nsym, hmaxw, nsub, tiles = int(h[36]), int(h[38]), int(h[39]), int(h[7])
+    nsym, hmaxw, nsub, tiles, nkb = int(h[36]), int(h[38]), int(h[39]), int(h[7]), int(h[23])
     tw = -(-tiles // min(tiles, 256))
     bufw = (hmaxw + 20 + 3) // 4 * 4
     static = 256 * 64 * 4 + 64
     for sub in (True, False):
         if sub and nsub > 64:
             continue
-        aux = 256 * max(nsub, 1) * 4 if sub else ((nsym + 1) // 2 + 3) // 4 * 4 * 4
-        for g in (2, 1):
-            if static + K * 2 + aux + (tw + 15) * 64 + 16 * g * bufw * 4 <= 160 * 1024:
+        aux = 256 * nsub * 4 if sub else ((nsym + 1) // 2 + 3) // 4 * 4 * 4
+        fixed = K * 2 + aux + (tw + 15) * 64 + ((tw * nkb + 4) & ~3) * 4
+        for g in (3, 2, 1):
+            if static + fixed + 16 * g * bufw * 4 <= 160 * 1024:
                 return sub, g
     return None
 
@@ -471,8 +472,9 @@ _CODE16 = ([0] + [v for a in range(1, 1025) for v in (-a, a)], [1] + [16] * 2048
 
 
 @pytest.mark.parametrize("code,p_zero,M,K,path", [
-    (_CODE13, 0.85, 40, 512, (False, 2)),   # canonical search, two blocks side by side
+    (_CODE13, 0.85, 40, 512, (False, 3)),   # canonical search, three blocks side by side
     (_CODE13, 0.10, 24, 512, (False, 1)),   # canonical search, large blocks: one at a time
+    (_CODE16, 0.55, 24, 512, (True, 2)),    # second-level tables, blocks of ~7.8 bits per weight: two
     (_CODE16, 0.10, 24, 512, (True, 1)),    # second-level tables, large blocks
 ])
 def test_hptq_fallback_paths(torch, code, p_zero, M, K, path):
