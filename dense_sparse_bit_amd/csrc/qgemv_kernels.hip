@@ -1366,8 +1366,9 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
   // 32 (l / 16) + 8i .. +7 of the K-block; rows past NB read out of range
   const rsrc_t rxb = make_rsrc(x, NB == 1 ? 0u : (uint32_t)(NB * K) * 2u);
   const int xrow = NB > 1 && (lane & 15) < NB ? (lane & 15) * K : -1;
-  constexpr int XP = NB == 1 ? 1 : 4;
+  constexpr int XP = NB == 1 ? 1 : 2;  // x pieces in flight per chain
   u32x4_t pre[G], xq[G][XP];
+  int xk[G];  // the chain's K offset in x (its block's first column of this lane)
   uint32_t lbn[G], stn0[G], stn1[G];
 #pragma unroll
   for (int c = 0; c < G; ++c) {
@@ -1428,12 +1429,11 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
       }
       st0[c] = stn0[c];
       st1[c] = stn1[c];
-      if constexpr (NB > 1) {  // from L2; first used after 8 codewords
-        const int k0 = (bb - (bb / nkb) * nkb) * kBlockK + 32 * (lane >> 4);
+      if constexpr (NB > 1) {  // pieces 0 and 1 from L2 now, piece i + 2 after MFMA i
+        xk[c] = xrow < 0 || bb >= b1 ? -1 : xrow + (bb - (bb / nkb) * nkb) * kBlockK + 32 * (lane >> 4);
 #pragma unroll
         for (int i = 0; i < XP; ++i)
-          xq[c][i] = __builtin_amdgcn_raw_buffer_load_b128(
-              rxb, xrow < 0 || bb >= b1 ? (int)kOutOfRange : (xrow + k0 + 8 * i) * 2, 0, 0);
+          xq[c][i] = __builtin_amdgcn_raw_buffer_load_b128(rxb, xk[c] < 0 ? (int)kOutOfRange : (xk[c] + 8 * i) * 2, 0, 0);
       }
     }
     prefetch(r0 + G, false);
@@ -1489,9 +1489,13 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
             const int bb = r0 + c, kb = bb - (bb / nkb) * nkb;
             bx = *(const half8_t*)(xs + kb * kBlockK + sl + j - 6);
           } else {
-            bx = __builtin_bit_cast(half8_t, xq[c][NB == 1 ? 0 : (j >> 3)]);
+            bx = __builtin_bit_cast(half8_t, xq[c][(j >> 3) & 1]);
           }
           blk[c] = mfma(h8(qh[c][0], qh[c][1], qh[c][2], qh[c][3]), bx, blk[c]);
+          if constexpr (NB > 1)
+            if ((j >> 3) + 2 < 4)
+              xq[c][(j >> 3) & 1] = __builtin_amdgcn_raw_buffer_load_b128(
+                  rxb, xk[c] < 0 ? (int)kOutOfRange : (xk[c] + 8 * ((j >> 3) + 2)) * 2, 0, 0);
         }
       }
     }
@@ -1759,8 +1763,8 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
 }
 
 // HPTQ: one workgroup per CU over its tile range; G = 3 blocks decoded side
-// by side per wave (2 at batch 8/16) where their buffers fit in LDS, else
-// fewer.  Long codewords
+// by side per wave where their buffers fit in LDS and their registers fit
+// without spilling, else fewer.  Long codewords
 // go through the second-level tables where they fit in LDS, else through the
 // canonical search.  x sits in LDS at batch 1 and is read from L2 at 8/16.
 template <int G, bool SUB, int NB>
@@ -1792,14 +1796,18 @@ hipError_t launch_huff_nb(const qgemv_plan* p, const uint16_t* x, float* y, hipS
     if (sub && h.hsub > (uint32_t)kHuffMaxSub) continue;
     const size_t fixed = (NB == 1 ? (size_t)h.K * 2 : 0) + aux + (tw + 15) * 16 * NB * 4 +
                          ((tw * (size_t)h.nkb + 4) & ~(size_t)3) * 4;
-    for (int g = NB == 1 ? 3 : 2; g >= 1; --g) {  // three chains' x pieces would spill at batch 8/16
+    // three chains spill registers at batch 16, and with the canonical search at batch 8
+    for (int g = NB == 1 || (NB == 8 && sub) ? 3 : 2; g >= 1; --g) {
       size_t lds = fixed + (size_t)kWaves * g * bufw * 4;
       if (lds + table > kLdsBytes) continue;
       if (lds + table < kOneWorkgroupLds) lds = kOneWorkgroupLds - table;
-      if constexpr (NB == 1)
-        if (g == 3)
+      if (g == 3) {
+        if constexpr (NB == 1)
           return sub ? launch_huff_g<3, true, NB>(p, x, y, grid, lds, bufw, st)
                      : launch_huff_g<3, false, NB>(p, x, y, grid, lds, bufw, st);
+        else if constexpr (NB == 8)
+          return launch_huff_g<3, true, NB>(p, x, y, grid, lds, bufw, st);
+      }
       if (sub)
         return g == 2 ? launch_huff_g<2, true, NB>(p, x, y, grid, lds, bufw, st)
                       : launch_huff_g<1, true, NB>(p, x, y, grid, lds, bufw, st);
