@@ -319,7 +319,7 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kWaves = 16;
 constexpr uint32_t kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), no wait on the other counters
 
-template <int FMT, int BITS, int CH, int NR, int NB>
+template <int FMT, int BITS, int CH, int NR, int NB, bool XST>
 __global__ void __launch_bounds__(64 * kWaves)
 k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ row_ptr,
          const uint32_t* __restrict__ entries, const int32_t* __restrict__ boff, const uint32_t* __restrict__ bent,
@@ -376,6 +376,10 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
   uint32_t* lut_lds = (uint32_t*)(rp_lds + rp_n);  // 16-byte aligned
   uint32_t* ent_lds = lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0);  // batch 1
   uint16_t* otile = (uint16_t*)ent_lds + 2048 * w;  // batch NB: this wave's outlier tile, A-operand order
+  // Batch NB with XST: this wave's x stage, [16 batch rows][16 pieces of 8
+  // columns] FP16, piece c of row r at slot c ^ r, so that the row-contiguous
+  // stores and the B-operand reads both spread over all banks.
+  uint16_t* xstage = (uint16_t*)ent_lds + 2048 * (kWaves + w);
 
   const rsrc_t rc = make_rsrc(codes, codes_bytes);
   const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
@@ -480,7 +484,20 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
     } else {
       sb[u][0] = sb[u][1] = 0;
     }
-    if constexpr (!B1) {
+    if constexpr (!B1 && XST) {
+      // x of the K-block, batch rows 4 s2 .. 4 s2 + 3 per instruction, 256
+      // contiguous bytes each: lane l takes row 4 s2 + l / 16, columns
+      // 8 (l % 16) .. +7 (rows past NB are not loaded; their MFMA columns are
+      // never stored).
+      const int kbl = g - (g / nkb) * nkb;
+      const bool ok = in && 128 * kbl + 8 * (lane & 15) < K;
+#pragma unroll
+      for (int s2 = 0; s2 < NB / 4; ++s2)
+        xr[u][s2] = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, ok ? (int)((uint32_t)(4 * s2 + (lane >> 4)) * (uint32_t)K * 2u + 256u * (uint32_t)kbl + 16u * (uint32_t)(lane & 15))
+                   : (int)kOutOfRange,
+            0, 0);
+    } else if constexpr (!B1) {
       const int kbl = g - (g / nkb) * nkb;
       const uint32_t xo = in && xrow != kOutOfRange && 128 * kbl + xq < K ? xrow + 256u * (uint32_t)kbl : kOutOfRange;
 #pragma unroll
@@ -635,11 +652,25 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
                                       perm(sb[sl][0], sb[sl][1], 0x07060302u)};
               decode_chunk<FMT, BITS>(cb[sl], st, tab, am);
             }
+            u32x4_t xb4[4];  // batch NB: the B operands of the four steps
+            if constexpr (!B1 && XST) {
+#pragma unroll
+              for (int s2 = 0; s2 < NB / 4; ++s2) {
+                const int r = 4 * s2 + (lane >> 4);
+                *(u32x4_t*)(xstage + 128 * r + 8 * ((lane & 15) ^ r)) = xr[sl][s2];
+              }
+              const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) xb4[s2] = *(const u32x4_t*)(xstage + 128 * n + 8 * ((4 * q + s2) ^ n));
+            } else if constexpr (!B1) {
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) xb4[s2] = xr[sl][s2];
+            }
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
               half8_t bx;
               if constexpr (B1) bx = *(const half8_t*)(xb + kb * kBlockK + 8 * s2);
-              else bx = __builtin_bit_cast(half8_t, xr[sl][s2]);
+              else bx = __builtin_bit_cast(half8_t, xb4[s2]);
               acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx, acc);
               if constexpr (!F::lut)
                 acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx, acc);
@@ -668,7 +699,7 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
                   const u32x4_t a = ((const u32x4_t*)otile)[s2 * 64 + lane];
-                  acc = mfma(h8(a[0], a[1], a[2], a[3]), __builtin_bit_cast(half8_t, xr[sl][s2]), acc);
+                  acc = mfma(h8(a[0], a[1], a[2], a[3]), __builtin_bit_cast(half8_t, xb4[s2]), acc);
                 }
                 if (n <= 64) {
                   if (lane < n) otile[oa] = 0;
@@ -1622,17 +1653,18 @@ size_t stream_lds_per_tile(const BlobHeader& h, int nb, int ch) {
 
 // LDS besides the per-tile parts and the CSR entries: batch 1, x with 16 zero
 // bytes and the spare row_ptr slots; batch NB, offset padding and the 16
-// waves' 4 KiB outlier tiles.
-size_t stream_lds_extra(const BlobHeader& h, int nb) {
-  return nb == 1 ? (size_t)h.Kp * 2 + 16 + 16 : 32 + (size_t)kWaves * 4096;
+// waves' 4 KiB outlier tiles (and 4 KiB x stages with xst).
+size_t stream_lds_extra(const BlobHeader& h, int nb, bool xst) {
+  return nb == 1 ? (size_t)h.Kp * 2 + 16 + 16 : 32 + (size_t)kWaves * 4096 * (xst ? 2 : 1);
 }
 
 // One workgroup per CU, more when the per-tile LDS of 256 workgroups would
 // not fit (batch 1 keeps at least 16 KiB for CSR entries) or, for batch NB,
 // a workgroup's block offsets would exceed 4096.
-int stream_grid(const BlobHeader& h, int nb, int ch) {
+int stream_grid(const BlobHeader& h, int nb, int ch, bool xst) {
   const size_t keep = nb == 1 ? 16 * 1024 : 0;
-  size_t max_tw = (kLdsBytes - stream_lds_extra(h, nb) - keep) / stream_lds_per_tile(h, nb, ch);
+  if (stream_lds_extra(h, nb, xst) + keep >= kLdsBytes) return 1 << 30;
+  size_t max_tw = (kLdsBytes - stream_lds_extra(h, nb, xst) - keep) / stream_lds_per_tile(h, nb, ch);
   if (max_tw > 32) max_tw = 32;
   if (nb > 1 && max_tw > (size_t)(4095 / h.nkb)) max_tw = (size_t)(4095 / h.nkb);
   if (max_tw < 1) max_tw = 1;
@@ -1641,18 +1673,26 @@ int stream_grid(const BlobHeader& h, int nb, int ch) {
   return g > need ? g : need;
 }
 
-size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int ch) {
+size_t stream_lds_fixed(const BlobHeader& h, int grid, int nb, int ch, bool xst) {
   const size_t tw = (size_t)((h.tiles + grid - 1) / grid);
-  return stream_lds_extra(h, nb) + tw * stream_lds_per_tile(h, nb, ch);
+  return stream_lds_extra(h, nb, xst) + tw * stream_lds_per_tile(h, nb, ch);
 }
 
-template <int FMT, int BITS, int NB>
-hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+// Batch NB stages x through LDS (contiguous loads) when the stages fit beside
+// the per-tile parts without needing more workgroups.
+bool stream_xst(const BlobHeader& h, int nb, int ch) {
+  if (nb == 1) return false;
+  const int g = stream_grid(h, nb, ch, true);
+  return g == stream_grid(h, nb, ch, false) && stream_lds_fixed(h, g, nb, ch, true) <= kLdsBytes;
+}
+
+template <int FMT, int BITS, int NB, bool XST>
+hipError_t launch_stream_x(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
   constexpr int CH = NB == 1 ? 2 : 3;  // K-blocks per chunk
   constexpr int NR = 1;                // chunks in flight per wave
   const BlobHeader& h = p->h;
-  const int grid = stream_grid(h, NB, CH);
-  const size_t fixed = stream_lds_fixed(h, grid, NB, CH);
+  const int grid = stream_grid(h, NB, CH, XST);
+  const size_t fixed = stream_lds_fixed(h, grid, NB, CH, XST);
   if (fixed > kLdsBytes) return hipErrorInvalidValue;
   // Batch 1 gives the rest of LDS (up to 64 KiB) to the CSR entries.
   size_t cap = 0;
@@ -1665,17 +1705,27 @@ hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipSt
   // More than half of LDS keeps a second workgroup off the CU: one per CU.
   if (lds < kOneWorkgroupLds) lds = kOneWorkgroupLds;
   // once per instantiation (thread-safe static initialisation)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, CH, NR, NB>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_stream<FMT, BITS, CH, NR, NB, XST>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
   const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
   const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
-  hipLaunchKernelGGL((k_stream<FMT, BITS, CH, NR, NB>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
+  hipLaunchKernelGGL((k_stream<FMT, BITS, CH, NR, NB, XST>), dim3(grid), dim3(64 * kWaves), lds, st, p->blob + h.off_codes,
                      (const uint32_t*)(p->blob + h.off_meta), (const int32_t*)(p->blob + h.off_rowptr),
                      (const uint32_t*)(p->blob + h.off_entries), (const int32_t*)(p->blob + h.off_boff),
                      (const uint32_t*)(p->blob + h.off_bent), x, y, h.M, h.K, h.Kp, h.nkb, h.tiles, codes_bytes,
                      meta_bytes, (int)h.nnz, (int)(cap / 4), h.group_size > 0 ? h.group_size : 16);
   return hipGetLastError();
+}
+
+template <int FMT, int BITS, int NB>
+hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
+  if constexpr (NB == 1) {
+    return launch_stream_x<FMT, BITS, NB, false>(p, x, y, st);
+  } else {
+    return stream_xst(p->h, NB, 3) ? launch_stream_x<FMT, BITS, NB, true>(p, x, y, st)
+                                   : launch_stream_x<FMT, BITS, NB, false>(p, x, y, st);
+  }
 }
 
 // LDS of the x-resident batched kernel apart from the CSR entries: x, partial
