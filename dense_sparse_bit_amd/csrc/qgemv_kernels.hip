@@ -1323,10 +1323,10 @@ k_huff(const uint32_t* __restrict__ words, const uint16_t* __restrict__ steps, c
 
   // LDS: first-level table [kHuffTable][64] (static, at address 0: entry e of
   //      lane l at e * 64 + l, so that a wave's 64 reads fall in 64 banks)
-  //      | xs [K] FP16 (batch 1) | aux | slots [TW+15][16 rows][NB] | code buffers [16][G][bufw];
+  //      | xs [K] FP16 (batch 1) | aux | slots [TW+15][16 rows][NB]
+  //      | block word offsets hidx[T0 * nkb .. T1 * nkb] (padded) | code buffers [16][G][bufw];
   //      aux: the second-level tables [nsub][kHuffSub] (SUB), else the
-  //      integers [nsym] FP16 (padded).  At batch 8/16 x stays in L2.  Then
-  //      the workgroup's block word offsets hidx[T0 * nkb .. T1 * nkb] (padded).
+  //      integers [nsym] FP16 (padded).  At batch 8/16 x stays in L2.
   __shared__ uint32_t tab[kHuffTable * 64];
   const int xsw = NB == 1 ? K / 2 : 0;
   uint16_t* xs = (uint16_t*)lds;

@@ -511,3 +511,20 @@ def test_hptq_single_integer(torch, M, K):
     y1 = run_b1(torch, plan, x16)
     assert np.array_equal(y1, np.zeros_like(y1))
     plan.close()
+
+
+def test_hptq_create_rejects_inconsistent_headers(torch):
+    """qgemv_create checks the blob's HPTQ fields it cannot derive from the shape."""
+    from oracle import hptq
+    W, _ = make_weights(WORKLOADS["mlp7b_lut3"], 0, 20, 256)
+    enc = hptq.encode(W, 128, 3.125)
+    good = qgemv.repack(enc)
+    plan = qgemv.QGemv(enc, blob=good)  # the unmodified blob binds
+    plan.close()
+    for field, value in ((38, 6), (38, 1 << 20), (39, 0), (39, 1 << 20)):  # hmaxw not a multiple of 4 / too big; hsub
+        bad = good.copy()
+        bad[:256].view(np.int32)[field] = value
+        _say(f"[gpu] hptq header field {field} = {value}")
+        with pytest.raises(qgemv.QgemvError) as err:
+            qgemv.QGemv(enc, blob=bad)
+        assert err.value.status == -5  # QGEMV_ERR_SIZE
