@@ -1107,9 +1107,10 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   int* rp_lds = (int*)(csr + TW * 16);
   int* group_ctr = rp_lds + ((TW * 16 + 4) & ~3);
 
-  // Prologue.  What goes to LDS is loaded first, then the code ring; storing
-  // the staged pieces waits for them alone, and the barrier (LDS only) lets
-  // the ring loads run on into the stream.
+  // Prologue.  What goes to LDS is loaded first and waited for before the
+  // code ring is issued, so that these few loads do not queue behind every
+  // CU's ring at the start; the barrier (LDS only) then lets the ring loads
+  // run on into the stream.
   const rsrc_t rr = make_rsrc(row_ptr, (uint32_t)(M + 1) * 4);
   const int rpn = threadIdx.x <= TW * 16 ? __builtin_amdgcn_raw_buffer_load_b32(
                                                rr, min(T0 * 16 + (int)threadIdx.x, M) * 4, 0, 0)
@@ -1140,6 +1141,8 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
     xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, piece < xpieces ? piece * 16 : (int)kOutOfRange, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the ring loads behind the staged ones
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);  // the staged loads have landed
+  asm volatile("" ::"v"(la[0]), "v"(lb[0]), "v"(la[1]), "v"(lb[1]), "v"(xv[0]), "v"(xv[1]));
   // The code ring.  Unit v: region g = v / P, quarter-block v % P; lanes of
   // tiles past T1 fall outside the resource and read 0.
   const rsrc_t rc = make_rsrc(codes, (uint32_t)T1 * (uint32_t)nkb * 1024u);
@@ -1152,9 +1155,6 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   u32x4_t ring[R];
 #pragma unroll
   for (int s = 0; s < R; ++s) ring[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)uoff(u0 + s), 0, kNonTemporal);
-  // The table loads are used only for regions that exist; this use keeps
-  // them ahead of the ring (the wait it implies is the one below).
-  asm volatile("" ::"v"(la[0]), "v"(lb[0]), "v"(la[1]), "v"(lb[1]));
 
   // x in pair order: (0,4,1,5,2,6,3,7) in each 8-column group.  A piece past
   // x goes to the first 16 bytes after it (partial slot 0, which is written
