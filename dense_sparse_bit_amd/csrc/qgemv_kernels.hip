@@ -917,10 +917,12 @@ k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
       sb[u][0] = sb[u][1] = 0;
     }
   };
+  // x, the tables and the CSR run land before the code ring is issued, so
+  // that they do not queue behind every CU's ring at the start.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
 #pragma unroll
   for (int u = 0; u < R; ++u) issue(u, b0 + u < b1 ? b0 + u : -1);
 
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   if ((int)threadIdx.x <= TW * 16) rp_lds[threadIdx.x] = rpn;
   if constexpr (F::lut) {
     if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
