@@ -1052,9 +1052,15 @@ k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   __syncthreads();
   for (int i = threadIdx.x; i < nrows * NB; i += 64 * kWaves) {
     const int r = i / NB, n = i % NB, t = r >> 4;
+    // Every slot is read before the first add (slots past the runs are in
+    // bounds and dropped by the select), so the reads overlap instead of
+    // waiting one by one inside a branch.
+    float s[kWaves];
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) s[u] = slots[((u + t) * 16 + (r & 15)) * NB + n];
     float v = 0.f;
-    for (int u = 0; u < kWaves; ++u)
-      if (runs[2 * u] <= t && t <= runs[2 * u + 1]) v += slots[((u + t) * 16 + (r & 15)) * NB + n];
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) v = runs[2 * u] <= t && t <= runs[2 * u + 1] ? v + s[u] : v;
     y[(size_t)n * M + T0 * 16 + r] = v + csr[i];
   }
 }
@@ -1265,10 +1271,14 @@ k_pair(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
   __syncthreads();
   for (int r = threadIdx.x; r < nrows; r += 64 * kWaves) {
     const int g = r >> 6;  // local row r = 64 g + 16 t + m
+    float s[kWaves];  // all reads first, then the adds in wave order
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) s[u] = slots[(u + g) * 64 + (r & 63)];
     float v = 0.f;
+#pragma unroll
     for (int u = 0; u < kWaves; ++u) {
       const int c0 = run_bound(u), c1 = run_bound(u + 1);
-      if (c0 < c1 && c0 < (g + 1) * P && c1 > g * P) v += slots[(u + g) * 64 + (r & 63)];
+      v = c0 < c1 && c0 < (g + 1) * P && c1 > g * P ? v + s[u] : v;
     }
     y[T0 * 16 + r] = v + csr[r];
   }
