@@ -776,9 +776,14 @@ k_stream(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, c
 #pragma unroll
           for (int u = 0; u < 4; ++u) v = dot2(e[u] >> 16, xv[u], v);
         }
-        for (; p < pm; p += 16) {
-          const uint32_t e = ent_lds[p - A0];
-          v = dot2(e >> 16, (uint32_t)x_lds[e & 0xFFFFu], v);
+        {  // the last three or fewer, read together (masked reads stay in LDS)
+          uint32_t e[3], xv[3];
+#pragma unroll
+          for (int u = 0; u < 3; ++u) e[u] = ent_lds[p + 16 * u < pm ? p + 16 * u - A0 : 0];
+#pragma unroll
+          for (int u = 0; u < 3; ++u) xv[u] = x_lds[p + 16 * u < pm ? e[u] & 0xFFFFu : 0u];
+#pragma unroll
+          for (int u = 0; u < 3; ++u) v = p + 16 * u < pm ? dot2(e[u] >> 16, xv[u], v) : v;
         }
         for (int p = max(p0, Acap) + sl; p < p1; p += 16) {
           const uint32_t e = entries[p];
