@@ -194,6 +194,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--copy-mb", type=int, default=0, help="also time a plain device copy of this many MiB")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured streaming-read ceiling")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -278,6 +279,18 @@ def main():
         out["mfma"] = {"tflops": round(tf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
                        "util": round(tf / MFMA_F16_PEAK_TFLOPS, 5),
                        "note": "dense flops 2*B*M*K at fp16 MFMA peak; the path stays HBM-bound"}
+    if not a.no_ceiling:
+        # The streaming-read rate of this GPU, measured in the same run: the
+        # library's read probe (16-byte non-temporal loads) over 1 GiB.
+        n = 1 << 30
+        buf = torch.full((n,), 7, dtype=torch.uint8, device=dev)
+        sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+        ms_r = time_graph(torch, lambda i: qgemv.read_probe(buf, sink, stream=stream), 20, 3, stream,
+                          use_graph=False)
+        ceil_gbs = n / (ms_r * 1e-3) / 1e9
+        out["roofline"]["measured_read_ceiling"] = {"GBs": round(ceil_gbs, 1), "frac": round(gbs / ceil_gbs, 4),
+                                                    "kernel": "qgemv_read_probe over 1 GiB, eager"}
+        del buf, sink
     if a.copy_mb:
         n = a.copy_mb << 20
         src_t = torch.ones(n // 4, dtype=torch.float32, device=dev)

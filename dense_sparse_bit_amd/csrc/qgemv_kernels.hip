@@ -1912,6 +1912,32 @@ hipError_t launch_unpack(const qgemv_plan* p, uint8_t* out, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Streaming-read probe (measurement only, none of the method's arithmetic):
+// reads `bytes` (a multiple of 16, at most 1 GiB) once with 16-byte
+// non-temporal buffer loads, four in flight per lane, and XORs the dwords it
+// read into one word per thread.  Thread t reads the 16-byte pieces t,
+// t + T, t + 2T, ... (T threads in the grid), so sink[t] is the XOR of those
+// pieces' dwords.  It gives the read ceiling the GEMV kernels are held against.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_read_probe(const uint8_t* __restrict__ src, uint32_t bytes, uint32_t* __restrict__ sink) {
+  const rsrc_t r = make_rsrc(src, bytes);
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x, step = gridDim.x * 256u * 16u;
+  uint32_t acc = 0;
+  for (uint32_t i = t * 16u; i < bytes; i += 4u * step) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t o = i + (uint32_t)u * step;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(o < bytes ? o : kOutOfRange), 0, kNonTemporal);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  sink[t] = acc;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return QGEMV_OK;
   qgemv_set_hip_error((int)e);
@@ -1981,6 +2007,15 @@ int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream) {
     e = h->h.bits == 4 ? launch_unpack<QGEMV_FMT_UNIFORM, 4>(h, codes_dev, st)
                        : launch_unpack<QGEMV_FMT_UNIFORM, 3>(h, codes_dev, st);
   return hip_status(e);
+}
+
+int qgemv_read_probe(const void* src_dev, uint64_t bytes, uint32_t* sink_dev, int32_t sink_words, void* stream) {
+  if (!src_dev || !sink_dev || (uintptr_t)src_dev % 16 || (uintptr_t)sink_dev % 4) return QGEMV_ERR_INVALID_ARG;
+  if (bytes == 0 || bytes % 16 || bytes > (1ull << 30) || sink_words < 256) return QGEMV_ERR_INVALID_ARG;
+  const int grid = sink_words / 256 < 1024 ? sink_words / 256 : 1024;
+  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)src_dev,
+                     (uint32_t)bytes, sink_dev);
+  return hip_status(hipGetLastError());
 }
 
 int qgemv_destroy(qgemv_handle h) {

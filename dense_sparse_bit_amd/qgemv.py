@@ -31,6 +31,16 @@ STATUS = {0: "QGEMV_OK", -1: "QGEMV_ERR_INVALID_ARG", -2: "QGEMV_ERR_MALFORMED_C
           -3: "QGEMV_ERR_UNSUPPORTED", -4: "QGEMV_ERR_HIP", -5: "QGEMV_ERR_SIZE"}
 
 
+
+def read_probe(src, sink, stream=None):
+    """Enqueue one non-temporal read of the device tensor `src` (its bytes) into
+    per-thread XOR words in the int32/uint32 device tensor `sink`; measurement
+    only (the streaming-read ceiling)."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    s = (stream or torch.cuda.current_stream(src.device)).cuda_stream
+    _check(lib().qgemv_read_probe(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), s), "qgemv_read_probe")
+
 class QgemvError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -68,11 +78,12 @@ def lib() -> ctypes.CDLL:
     L.qgemv_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     L.qgemv_debug_unpack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.qgemv_destroy.argtypes = [ctypes.c_void_p]
+    L.qgemv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     L.qgemv_error_string.argtypes = [ctypes.c_int]
     L.qgemv_error_string.restype = ctypes.c_char_p
     L.qgemv_last_hip_error.argtypes = []
     for f in ("qgemv_packed_size", "qgemv_repack", "qgemv_unpack_host", "qgemv_create", "qgemv_run",
-              "qgemv_debug_unpack", "qgemv_destroy", "qgemv_last_hip_error"):
+              "qgemv_debug_unpack", "qgemv_read_probe", "qgemv_destroy", "qgemv_last_hip_error"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -187,6 +187,20 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
  */
 int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream);
 
+/*
+ * Measurement utility, not an operation of the method: enqueue one read of
+ * src_dev[0 .. bytes) (device memory, 16-byte aligned; bytes a multiple of 16,
+ * 1 .. 2^30) with 16-byte non-temporal loads, and write one uint32 per thread
+ * to sink_dev (device memory, 4-byte aligned, sink_words >= 256 words; the
+ * grid has min(1024, sink_words / 256) workgroups of 256 threads, T threads
+ * in all).  sink_dev[t] is the XOR of the dwords of the 16-byte pieces t,
+ * t + T, t + 2T, ... of src_dev, so the read can be checked.  Timing it gives
+ * the streaming-read rate of the GPU, the ceiling the GEMV is compared with.
+ * Errors: INVALID_ARG (null or misaligned pointer, bytes or sink_words out of
+ * range), HIP (launch failure).
+ */
+int qgemv_read_probe(const void* src_dev, uint64_t bytes, uint32_t* sink_dev, int32_t sink_words, void* stream);
+
 /* Release the plan (host memory only).  NULL is accepted. */
 int qgemv_destroy(qgemv_handle h);
 

@@ -17,7 +17,7 @@ from synth import WORKLOADS, make_weights, make_x, outlier_count
 def test_library_exports_every_declared_symbol():
     L = qgemv.lib()
     names = qgemv.header_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
 

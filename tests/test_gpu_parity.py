@@ -528,3 +528,30 @@ def test_hptq_create_rejects_inconsistent_headers(torch):
         with pytest.raises(qgemv.QgemvError) as err:
             qgemv.QGemv(enc, blob=bad)
         assert err.value.status == -5  # QGEMV_ERR_SIZE
+
+
+@pytest.mark.gpu
+def test_read_probe_reads_every_byte(torch):
+    """The read probe used for the measured ceiling: sink[t] must be the XOR of
+    the dwords of pieces t, t + T, ... (a ragged size, not a multiple of T)."""
+    from dense_sparse_bit_amd import qgemv
+    rng = np.random.default_rng(11)
+    nbytes = 3 * (1 << 20) + 48
+    host = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    src = torch.from_numpy(host).cuda()
+    for words in (256, 1024 * 256):
+        sink = torch.zeros(words, dtype=torch.int32, device="cuda")
+        qgemv.read_probe(src, sink)
+        torch.cuda.synchronize()
+        T = min(1024, words // 256) * 256
+        piece = np.bitwise_xor.reduce(host.view(np.uint32).reshape(-1, 4), axis=1)
+        want = np.zeros(T, np.uint32)
+        for t in range(min(T, len(piece))):
+            want[t] = np.bitwise_xor.reduce(piece[t::T])
+        got = sink.cpu().numpy().view(np.uint32)[:T]
+        assert np.array_equal(got, want)
+    bad = torch.zeros(256, dtype=torch.int32, device="cuda")
+    with pytest.raises(qgemv.QgemvError):
+        qgemv.read_probe(src[:40], bad)  # 40 bytes: not a multiple of 16
+    with pytest.raises(qgemv.QgemvError):
+        qgemv.read_probe(src, bad[:128])  # fewer than 256 sink words
