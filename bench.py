@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--copy-mb", type=int, default=0, help="also time a plain device copy of this many MiB")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured streaming-read ceiling")
+    ap.add_argument("--read-probe-mb", type=float, default=0.0,
+                    help="only time the read probe over windows of this many MB (rotated through 2 GiB)")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -212,6 +214,19 @@ def main():
     torch.cuda.set_device(dev)
     B = a.batch or DEFAULT_BATCH.get(a.workload, 1)
     stream = torch.cuda.Stream(device=dev)
+
+    if a.read_probe_mb:
+        # Plain streaming reads of one layer's size: distinct windows of a
+        # 2 GiB buffer, so every launch reads from HBM, one HIP-graph replay.
+        w = int(a.read_probe_mb * 1e6) // 16 * 16
+        big = torch.full((2 << 30,), 7, dtype=torch.uint8, device=dev)
+        nwin = (2 << 30) // w
+        sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+        ms_p = time_graph(torch, lambda i: qgemv.read_probe(big[(i % nwin) * w:(i % nwin + 1) * w], sink,
+                                                             stream=stream), a.steps, a.warmup, stream)
+        print(json.dumps({"read_probe": {"bytes": w, "us": round(ms_p * 1e3, 3),
+                                         "GBs": round(w / (ms_p * 1e-3) / 1e9, 1), "windows": nwin}}), flush=True)
+        return
 
     per_layer, cpu_layers = [], []
     alg_total, ms_total = 0, 0.0
