@@ -209,7 +209,6 @@ def decode_rows(enc: dict, rows=None) -> np.ndarray:
     rows = np.arange(M) if rows is None else np.asarray(rows)
     sym, ln, codes = canonical_code(np.asarray(enc["huff_sym"], np.int64), np.asarray(enc["huff_len"], np.int64))
     rb = np.asarray(enc["row_bits"], np.int64)
-    sub = np.stack([rb[rows], rb[rows + 1]], axis=1).ravel()
     q = np.zeros((len(rows), K), dtype=np.int64)
     for k, i in enumerate(rows):
         q[k] = decode_stream(enc["stream"], rb[[i, i + 1]], K, sym, ln, codes)[0]
@@ -225,11 +224,15 @@ def decode(enc: dict) -> np.ndarray:
 
 
 def gemv(enc: dict, X16: np.ndarray, rows=None):
-    """y and its tolerance scale A (rows optional), fp64."""
-    D = decode(enc)
-    if rows is not None:
-        D = D[np.asarray(rows)]
+    """y and its tolerance scale A (rows optional), fp64.
+
+    There is no sparse part, so A[b, i] = sum_j |d_ij x[b, j]| (the tolerance
+    scale of the dense-and-sparse GEMV with an empty CSR).
+    """
+    from .gemv import tolerance_scale
+    D = decode(enc) if rows is None else decode_rows(enc, rows)
     x = np.asarray(X16).astype(np.float64)
     if x.ndim == 1:
         x = x[None, :]
-    return x @ D.T, np.abs(x) @ np.abs(D).T
+    none = np.zeros(0, np.int64)
+    return x @ D.T, tolerance_scale(x, D, none, none, np.zeros(0))

@@ -274,6 +274,128 @@ def test_sparse_scatter_equals_dense_product():
 
 
 # ---------------------------------------------------------------------------
+# Pin 3b: the acceptance test -- the tolerance scale A and the bound
+# ---------------------------------------------------------------------------
+def loop_weights(enc):
+    """Effective weights w_ij = d_ij + (CSR entry at (i, j)) in pure Python,
+    each code read bit by bit from the canonical bytes (no numpy arithmetic)."""
+    M, K, b = enc["M"], enc["K"], enc["bits"]
+    packed = np.asarray(enc["codes_packed"])
+    rp, ci, va = enc["row_ptr"], enc["col_idx"], enc["values"]
+    W = []
+    for i in range(M):
+        row = [int(v) for v in packed[i]]
+        w = []
+        for j in range(K):
+            q = 0
+            for t in range(b):
+                p = j * b + t
+                q |= ((row[p // 8] >> (p % 8)) & 1) << t
+            if enc["fmt"] == "uniform":
+                g = j // enc["group"]
+                d = float(enc["scales"][i, g]) * (q - float(enc["zeros"][i, g]))
+            elif enc["fmt"] == "bpdq":
+                c = [float(v) for v in enc["coefs"][i, j // enc["group"]]]
+                d = c[0] + sum(c[t + 1] for t in range(b) if (q >> t) & 1)
+            else:
+                d = float(enc["lut"][i, q])
+            w.append(d)
+        for p in range(int(rp[i]), int(rp[i + 1])):
+            w[int(ci[p])] += float(va[p])
+        W.append(w)
+    return W
+
+
+def loop_tolerance_scale(W, X16):
+    """A[b][i] = sum_j |w_ij * x_bj|, one term at a time."""
+    return np.array([[sum(abs(wij * float(xj)) for wij, xj in zip(wi, xb)) for wi in W] for xb in np.asarray(X16)])
+
+
+def check_tolerance_scale(enc, x):
+    _, A = gemv.gemv(enc, x)
+    Al = loop_tolerance_scale(loop_weights(enc), x)
+    return bool(np.all(np.abs(A - Al) <= 1e-12 * Al + 1e-300))
+
+
+@pytest.mark.parametrize("bits,fmt", [(3, "uniform"), (4, "uniform"), (3, "lut"), (4, "lut"), (3, "bpdq")])
+@pytest.mark.parametrize("n_out", [0, 5])
+def test_tolerance_scale_matches_loop(bits, fmt, n_out):
+    """A = sum_j |w_ij x_j| over the weights the product uses (dense decode plus CSR)."""
+    W, x, enc = _tiny_enc(bits, fmt, n_out, seed=bits * 10 + n_out + 100)
+    assert check_tolerance_scale(enc, x)
+    # also on a row subset, the way the GPU tests call it
+    rows = np.array([1, 4])
+    _, A = gemv.gemv_rows(enc, x, rows)
+    Al = loop_tolerance_scale(loop_weights(enc), x)[:, rows]
+    assert np.all(np.abs(A - Al) <= 1e-12 * Al)
+
+
+def test_tolerance_scale_catches_abs_of_product(monkeypatch):
+    """|sum_j w_ij x_j| in place of sum_j |w_ij x_j|."""
+    W, x, enc = _tiny_enc(4, "lut", 5, seed=31)
+
+    def abs_of_product(xx, D, loc, col, val):
+        Wd = np.array(D, copy=True)
+        np.add.at(Wd, (loc, col), val)
+        return np.abs(xx @ Wd.T)
+    monkeypatch.setattr(gemv, "tolerance_scale", abs_of_product)
+    assert not check_tolerance_scale(enc, x)
+
+
+def test_tolerance_scale_catches_dropped_sparse_term(monkeypatch):
+    W, x, enc = _tiny_enc(3, "uniform", 5, seed=32)
+    monkeypatch.setattr(gemv, "tolerance_scale", lambda xx, D, loc, col, val: np.abs(xx) @ np.abs(D).T)
+    assert not check_tolerance_scale(enc, x)
+
+
+def test_tolerance_scale_at_a_shared_position():
+    """A dense value 0.5 everywhere and a CSR entry -0.25 at column 3 (w = 0.25 there):
+    with x = 1, A = 31 * 0.5 + 0.25 = 15.75 (summing |d x| and |r x| apart would give 16.25)."""
+    K = 32
+    codes = np.full((1, K), 5, dtype=np.uint8)
+    lut = np.zeros((1, 16), np.float16)
+    lut[0, 5] = 0.5
+    enc = {"M": 1, "K": K, "bits": 4, "fmt": "lut", "group": 0, "codes": codes,
+           "codes_packed": pack.pack_bitstream(codes, 4), "lut": lut,
+           "row_ptr": np.array([0, 1], np.int32), "col_idx": np.array([3], np.int32),
+           "values": np.array([-0.25], np.float16)}
+    y, A = gemv.gemv(enc, np.ones((1, K), np.float16))
+    assert y[0, 0] == 15.75 and A[0, 0] == 15.75
+    x = np.ones((1, K), np.float16)
+    x[0, 3] = -1
+    y, A = gemv.gemv(enc, x)
+    assert y[0, 0] == 15.25 and A[0, 0] == 15.75
+
+
+def check_acceptance(within):
+    """The bound |y_test - y| <= 1e-4 A + 1e-6, at hand-computed points on both sides of it."""
+    A = np.array([0.0, 1.0, 2.0e4, 3.5])
+    y = np.array([0.25, -1.0, 7.0, 0.0])
+    bound = np.array([1e-6, 1.01e-4, 2.000001, 3.51e-4])
+    inside = y + bound * (1 - 1e-6)
+    outside = y - bound * (1 + 1e-6)
+    ok_in, worst_in = within(inside, y, A)
+    ok_out, worst_out = within(outside, y, A)
+    one_out = inside.copy()
+    one_out[1] = y[1] + 1.02e-4
+    ok_one, worst_one = within(one_out, y, A)
+    return (ok_in and worst_in <= 1.0 and not ok_out and worst_out > 1.0
+            and not ok_one and abs(worst_one - 1.02e-4 / 1.01e-4) < 1e-9)
+
+
+def test_acceptance_bound():
+    assert check_acceptance(gemv.within_tolerance)
+
+
+def test_acceptance_bound_catches_loose_rel():
+    assert not check_acceptance(lambda yt, yr, A: gemv.within_tolerance(yt, yr, A, rel=1e-3))
+
+
+def test_acceptance_bound_catches_missing_abs_term():
+    assert not check_acceptance(lambda yt, yr, A: gemv.within_tolerance(yt, yr, A, abs_=0.0))
+
+
+# ---------------------------------------------------------------------------
 # Pin 4: canonical bitstream
 # ---------------------------------------------------------------------------
 def check_bitstream_golden():
@@ -902,3 +1024,70 @@ def test_hptq_gemv_matches_plain_product_of_decoded_grid():
     y, A = hptq.gemv(enc, x)
     d = np.repeat(enc["scales"].astype(np.float64), 128, axis=1) * enc["q"]
     assert np.allclose(y, x.astype(np.float64) @ d.T, rtol=0, atol=1e-12)
+
+
+def string_prefix_decode(enc):
+    """Integers read from the stream by matching codeword strings (the
+    canonical codewords written out as '0'/'1' strings from the lengths)."""
+    sym, ln, codes = hptq.canonical_code(np.asarray(enc["huff_sym"], np.int64), np.asarray(enc["huff_len"], np.int64))
+    words = {format(int(c), f"0{int(l)}b"): int(s) for s, c, l in zip(sym, codes, ln)}
+    bits = "".join(format(int(b), "08b") for b in np.asarray(enc["stream"], np.uint8))
+    q = []
+    for i in range(enc["M"]):
+        p, row = int(enc["row_bits"][i]), []
+        while len(row) < enc["K"]:
+            w = ""
+            while w not in words:
+                w += bits[p]; p += 1
+            row.append(words[w])
+        assert p == int(enc["row_bits"][i + 1])
+        q.append(row)
+    return q
+
+
+def check_hptq_gemv(enc, x):
+    q = string_prefix_decode(enc)
+    s = np.asarray(enc["scales"]).astype(np.float64)
+    g = enc["group"]
+    Wl = [[float(s[i, j // g]) * q[i][j] for j in range(enc["K"])] for i in range(enc["M"])]
+    yl = np.array([[sum(w * float(v) for w, v in zip(wi, xb)) for wi in Wl] for xb in x])
+    Al = loop_tolerance_scale(Wl, x)
+    y, A = hptq.gemv(enc, x)
+    rows = np.array([enc["M"] - 1, 0, 3])
+    yr, Ar = hptq.gemv(enc, x, rows)
+    return bool(np.all(np.abs(y - yl) <= 1e-12 * Al) and np.all(np.abs(A - Al) <= 1e-12 * Al)
+                and np.all(np.abs(yr - yl[:, rows]) <= 1e-12 * Al[:, rows])
+                and np.all(np.abs(Ar - Al[:, rows]) <= 1e-12 * Al[:, rows]))
+
+
+def _hptq_tiny():
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, 6, 256)
+    enc = hptq.encode(W, 128, 3.125)
+    x = np.random.default_rng(4).standard_normal((2, 256)).astype(np.float16)
+    return enc, x
+
+
+def test_hptq_gemv_matches_string_decoder():
+    """y and A of the HPTQ oracle against a decoder that matches codeword strings."""
+    enc, x = _hptq_tiny()
+    assert check_hptq_gemv(enc, x)
+
+
+def test_hptq_gemv_catches_abs_of_product(monkeypatch):
+    enc, x = _hptq_tiny()
+    monkeypatch.setattr(gemv, "tolerance_scale", lambda xx, D, loc, col, val: np.abs(xx @ D.T))
+    assert not check_hptq_gemv(enc, x)
+
+
+def test_hptq_decode_rows_equals_whole_decode():
+    """Rows decoded one at a time from their row_bits equal the same rows of the whole decode."""
+    wl = WORKLOADS["mlp7b_lut3"]
+    W, _ = make_weights(wl, 0, 24, 256)
+    enc = hptq.encode(W, 128, 3.125)
+    full = hptq.decode(enc)
+    rng = np.random.default_rng(2)
+    for n in (1, 5, 24):
+        rows = rng.choice(24, size=n, replace=False)
+        assert np.array_equal(hptq.decode_rows(enc, rows), full[rows])
+        assert np.array_equal(gemv.decode_rows(dict(enc, fmt="hptq"), rows), full[rows])
