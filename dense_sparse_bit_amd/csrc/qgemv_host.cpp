@@ -602,14 +602,27 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes) {
   return QGEMV_OK;
 }
 
-int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out) {
+int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out, size_t codes_bytes) {
   if (!blob_host || !codes_out) return QGEMV_ERR_INVALID_ARG;
   if (bytes < sizeof(BlobHeader)) return QGEMV_ERR_SIZE;
   BlobHeader h;
   std::memcpy(&h, blob_host, sizeof(h));
   if (h.magic != kMagic || h.version != kVersion) return QGEMV_ERR_SIZE;
-  if (h.total_bytes > bytes) return QGEMV_ERR_SIZE;
   if (h.format == QGEMV_FMT_HPTQ) return QGEMV_ERR_UNSUPPORTED;
+  // Every field must be the one the repacker writes for the header's own
+  // shape, so the loop below stays inside the blob.
+  qgemv_weights shape{};
+  shape.M = h.M;
+  shape.K = h.K;
+  shape.bits = h.bits;
+  shape.format = h.format;
+  shape.group_size = h.format == QGEMV_FMT_LUT ? 16 : h.group_size;
+  shape.nnz = h.nnz;
+  if (qgemv_validate_shape(&shape) != QGEMV_OK) return QGEMV_ERR_SIZE;
+  const BlobHeader expect = make_header(h.M, h.K, h.bits, h.format, shape.group_size, h.nnz);
+  if (std::memcmp(&expect, &h, sizeof(h)) != 0) return QGEMV_ERR_SIZE;
+  if (h.total_bytes > bytes) return QGEMV_ERR_SIZE;
+  if ((uint64_t)h.M * (uint64_t)h.K > codes_bytes) return QGEMV_ERR_SIZE;
   const uint8_t* blob = (const uint8_t*)blob_host;
   const int chunk_bytes = 4 * h.bits;
   uint32_t c[32], dw[4] = {0, 0, 0, 0};

@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
     P = ctypes.POINTER
     L.qgemv_packed_size.argtypes = [P(Weights), P(ctypes.c_size_t)]
     L.qgemv_repack.argtypes = [P(Weights), ctypes.c_void_p, ctypes.c_size_t]
-    L.qgemv_unpack_host.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.qgemv_unpack_host.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]
     L.qgemv_create.argtypes = [P(ctypes.c_void_p), P(Weights), ctypes.c_void_p, ctypes.c_size_t]
     L.qgemv_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     L.qgemv_debug_unpack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -159,7 +159,7 @@ def repack(w: dict) -> np.ndarray:
 def unpack_host(blob: np.ndarray, M: int, K: int) -> np.ndarray:
     out = np.zeros((M, K), dtype=np.uint8)
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
-    _check(lib().qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data), "qgemv_unpack_host")
+    _check(lib().qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data, out.size), "qgemv_unpack_host")
     return out
 
 

@@ -147,13 +147,16 @@ int qgemv_repack(const qgemv_weights* w, void* dst_host, size_t bytes);
 
 /*
  * Host-side inverse of the code repacking: read a blob in host memory and
- * write the canonical codes, one uint8 per weight, to codes_out [M][K] (host).
- * For tests of the repacker without a GPU.  HPTQ blobs: UNSUPPORTED (their
- * integers do not fit one byte).
- * Errors: INVALID_ARG (null pointer), SIZE (blob shorter than its header says
- * or header not recognised), UNSUPPORTED.
+ * write the canonical codes, one uint8 per weight, to codes_out [M][K] (host,
+ * codes_bytes long; M and K are the blob header's).  For tests of the
+ * repacker without a GPU.  HPTQ blobs: UNSUPPORTED (their integers do not fit
+ * one byte).
+ * Errors: INVALID_ARG (null pointer), SIZE (blob shorter than its header says,
+ * header not recognised, any header field different from what the repacker
+ * writes for the header's own M, K, bits, format, group and nnz, or
+ * codes_bytes < M*K), UNSUPPORTED (an HPTQ blob).
  */
-int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out);
+int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out, size_t codes_bytes);
 
 /*
  * Bind a plan to a blob already copied to device memory (packed_dev, bytes,

@@ -187,11 +187,31 @@ def test_nnz_mismatch_and_small_buffers():
 def test_unpack_host_rejects_garbage():
     junk = np.zeros(512, dtype=np.uint8)
     out = np.zeros(16, dtype=np.uint8)
-    assert qgemv.lib().qgemv_unpack_host(junk.ctypes.data, junk.size, out.ctypes.data) == -5
-    assert qgemv.lib().qgemv_unpack_host(None, 0, out.ctypes.data) == -1
+    assert qgemv.lib().qgemv_unpack_host(junk.ctypes.data, junk.size, out.ctypes.data, out.size) == -5
+    assert qgemv.lib().qgemv_unpack_host(None, 0, out.ctypes.data, out.size) == -1
     w = _random_canonical("uniform", 3, 2, 64)
     blob = qgemv.repack(w)
-    assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size - 256, out.ctypes.data) == -5
+    assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size - 256, out.ctypes.data, out.size) == -5
+
+
+@pytest.mark.parametrize("fmt,bits", [("uniform", 3), ("lut", 4), ("bpdq", 3)])
+def test_unpack_host_rejects_inconsistent_header_fields(fmt, bits):
+    """A header whose fields are not the repacker's for its own shape is refused
+    (bits = 16 would otherwise copy 64-byte chunks into a 16-byte buffer)."""
+    w = _random_canonical(fmt, bits, 20, 256)
+    blob = qgemv.repack(w)
+    out = np.zeros((20, 256), dtype=np.uint8)
+    L = qgemv.lib()
+    assert L.qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data, out.size) == 0
+    assert np.array_equal(out, w["codes"])
+    # int32 words of the header: 4 bits, 5 format, 6 group, 7 tiles, 10 off_codes, 20 block_bytes, 23 nkb
+    for word, value in ((4, 16), (4, 5), (5, 7), (6, 48), (7, 3), (7, 1 << 30), (10, 1 << 28),
+                        (20, 64 * 4 * 16), (23, 64), (2, 1 << 20)):
+        bad = blob.copy()
+        bad[:256].view(np.int32)[word] = value
+        assert L.qgemv_unpack_host(bad.ctypes.data, bad.size, out.ctypes.data, out.size) == -5, (word, value)
+    # an output buffer one byte short of M*K
+    assert L.qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data, out.size - 1) == -5
 
 
 def test_run_and_create_argument_checks_need_no_gpu():
@@ -346,7 +366,7 @@ def test_hptq_validation():
     assert _status(bad) == INV
     blob = qgemv.repack(enc)
     out = np.zeros(4 * 256, np.uint8)
-    assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data) == UNS
+    assert qgemv.lib().qgemv_unpack_host(blob.ctypes.data, blob.size, out.ctypes.data, out.size) == UNS
 
 
 def test_hptq_blob_long_codewords():

@@ -6,8 +6,8 @@
 * Runs are bitwise deterministic and overwrite every output.
 
 Small cases are oracle-encoded from the workloads' weight laws at sizes that
-span several wave steps and a ragged tail; full-size cases use random arrays
-in the storage format and compare sampled rows.
+span several wave steps and a ragged tail.  Full sizes, every row, are in
+test_gpu_parity_full.py.  Outputs are framed by canary words.
 """
 
 import sys
@@ -16,8 +16,9 @@ import numpy as np
 import pytest
 
 from dense_sparse_bit_amd import qgemv
+from gpu_checks import run_framed
 from oracle import encode, gemv, pack
-from synth import WORKLOADS, layer_shape, make_format_inputs, make_weights, make_x, outlier_count
+from synth import WORKLOADS, make_format_inputs, make_weights, make_x, outlier_count
 
 pytestmark = pytest.mark.gpu
 
@@ -61,21 +62,14 @@ def oracle_case(name, M, K, layer=0):
     return _ENC[key]
 
 
-def run_b1(torch, plan, x16, canary=True):
-    x = torch.from_numpy(np.ascontiguousarray(x16[:1])).cuda()
-    y = torch.full((1, plan.M), float("nan"), dtype=torch.float32, device="cuda") if canary else None
-    y = plan.run(x, y)
-    torch.cuda.synchronize()
-    return y.cpu().numpy().astype(np.float64)
+def run_b1(torch, plan, x16):
+    """Batch-1 run on the first row of x16, into a NaN-filled y framed by canaries."""
+    return run_framed(torch, plan, x16[:1])
 
 
 def run_bn(torch, plan, x16):
-    """Batched run (B = rows of x16) into a NaN-filled y."""
-    x = torch.from_numpy(np.ascontiguousarray(x16)).cuda()
-    y = torch.full((x16.shape[0], plan.M), float("nan"), dtype=torch.float32, device="cuda")
-    y = plan.run(x, y)
-    torch.cuda.synchronize()
-    return y.cpu().numpy().astype(np.float64)
+    """Batched run (B = rows of x16), into a NaN-filled y framed by canaries."""
+    return run_framed(torch, plan, x16)
 
 
 def check_y(y_gpu, enc, x16, rows=None):
@@ -149,34 +143,6 @@ def test_small_ssqr(torch, name, M, K, budget):
     check_y(run_b1(torch, plan, x16), enc, x16)
     xb = make_x(wl, 8, K_, 0, M_)
     check_y(run_bn(torch, plan, xb), enc, xb)
-    plan.close()
-
-
-FULL_CASES = [
-    ("tiny_u4", 0), ("attn7b_u3", 0), ("mlp7b_lut3", 0), ("mlp70b_lut4", 0),
-    ("block7b_u3", 0), ("block7b_u3", 4), ("block7b_u3", 6), ("mlp7b_bpdq3", 0),
-]
-
-
-@pytest.mark.parametrize("name,layer", FULL_CASES)
-def test_full_size_sampled(torch, name, layer):
-    f = format_case(name, layer)
-    M, K = f["M"], f["K"]
-    _say(f"[gpu] full {name} layer={layer} M={M} K={K} nnz={f['row_ptr'][-1]}")
-    x16 = make_x(name, 1, K, layer, M)
-    plan = qgemv.QGemv(f)
-    rng = np.random.default_rng(123)
-    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.choice(M, size=min(M, 384), replace=False)]))
-    codes = plan.debug_unpack().cpu().numpy()
-    ref_codes = pack.unpack_bitstream(f["codes_packed"][rows], f["bits"], K)
-    assert np.array_equal(codes[rows], ref_codes)
-    y = run_b1(torch, plan, x16)
-    assert np.all(np.isfinite(y))
-    check_y(y, f, x16, rows)
-    # heaviest CSR rows too (C4 skew)
-    nnz_row = np.diff(f["row_ptr"])
-    heavy = np.argsort(-nnz_row, kind="stable")[:16]
-    check_y(y, f, x16, np.sort(heavy))
     plan.close()
 
 
@@ -323,24 +289,6 @@ def test_batched_oracle_encoded(torch, name, M, K, B):
     check_y(y1, enc, x16)
     y2 = run_bn(torch, plan, x16)
     assert np.array_equal(y1, y2), "not bitwise deterministic"
-    plan.close()
-
-
-@pytest.mark.parametrize("name,layer,B", [("mlp70b_lut4", 0, 8), ("block7b_u3", 0, 16), ("block7b_u3", 4, 16),
-                                          ("block7b_u3", 6, 16), ("mlp7b_bpdq3", 0, 8)])
-def test_batched_full_size_sampled(torch, name, layer, B):
-    f = format_case(name, layer)
-    M, K = f["M"], f["K"]
-    _say(f"[gpu] batched full {name} layer={layer} B={B} M={M} K={K} nnz={f['row_ptr'][-1]}")
-    x16 = make_x(name, B, K, layer, M)
-    plan = qgemv.QGemv(f)
-    y = run_bn(torch, plan, x16)
-    assert np.all(np.isfinite(y)), "output not fully written"
-    rng = np.random.default_rng(321)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, 256), replace=False)]))
-    check_y(y, f, x16, rows)
-    heavy = np.argsort(-np.diff(f["row_ptr"]), kind="stable")[:16]
-    check_y(y, f, x16, np.sort(heavy))
     plan.close()
 
 
