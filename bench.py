@@ -9,18 +9,25 @@ synthetic arrays in the storage format with the workload's shapes, code
 widths, FP16 tables and outlier structure, resident in HBM before timing
 starts.
 
-Distinct copies of each weight blob (>= 1 GiB in total) are cycled so that
-every step streams its weights from HBM rather than from the 256 MB
-last-level cache.  Each layer's timed region is one HIP-graph replay of
-exactly K launches, bracketed by device synchronisation and timed with HIP
-events recorded on the launch stream.
+Distinct copies of each weight blob (>= 1 GiB in total) are cycled, launch i
+reading copy i mod copies, and the timed replay starts at copy `steps`,
+after the warm-up's copies, so every step streams its weights from HBM
+rather than from the 256 MB last-level cache.  Each layer's timed region is one
+HIP-graph replay of exactly K launches, bracketed by device synchronisation
+and timed with HIP events recorded on the launch stream.
 
 Prints ONE JSON line.  `value` is effective GB/s: algorithmic bytes per step
 (packed codes, FP16 statistics or tables, CSR as FP16 value + int32 column +
 int32 row pointer, x, y; each counted once) divided by the mean step time.
+With the default workload the line also carries `targets`: both batch-1
+shapes that have a 70 %-of-8-TB/s target (28672x8192 LUT-4 and 11008x4096
+LUT-3), each next to a plain streaming read of the same number of bytes.
 
 --copy-mb N also times a plain elementwise copy of N MiB (a kernel of known
 traffic, used to calibrate the HBM byte counters of a profiler run).
+--trace-summary CSV prints median / p10 / p90 of the timed replays' launches
+in a rocprofv3 kernel trace (--output-format csv) of a bench.py run given the
+same --steps and --warmup.
 """
 
 from __future__ import annotations
@@ -36,6 +43,13 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+# The CPU baseline runs on every host thread this process may use; the BLAS
+# reads its thread count when numpy is first imported, so set it here (an
+# existing setting is kept).
+HOST_THREADS = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+    os.environ.setdefault(_v, str(HOST_THREADS))
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
@@ -117,70 +131,208 @@ def workload_layers(workload: str):
     return [(0, "w")]
 
 
-def cpu_baseline(layers: list, alg_bytes: int, target_s: float = 12.0):
-    """The oracle's unpack + decode + GEMV + SpMV, single thread, on a bounded row sample of every layer."""
+def host_description() -> dict:
+    """CPU model and the BLAS build and thread count numpy runs on."""
+    model = platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from threadpoolctl import threadpool_info
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    b = blas[0] if blas else {}
+    return {"cpu": model, "affinity_threads": HOST_THREADS,
+            "blas": f"{b.get('internal_api', '?')} {b.get('version', '?')} ({b.get('architecture', '?')}, "
+                    f"{b.get('threading_layer', '?')})",
+            "blas_threads": int(b.get("num_threads", 1))}
+
+
+def cpu_baseline(layers: list, alg_bytes: int, row_frac: float = 0.125, runs: int = 5):
+    """The oracle's unpack + decode + GEMV + SpMV (y only) on the host cores.
+
+    A seeded random 1/8 of every layer's rows, in row order; median of `runs`
+    runs after one warm-up, scaled to all rows.
+    """
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from oracle import gemv
+    host = host_description()
     rng = np.random.default_rng(7)
-    budget = target_s / len(layers)
     t_step, sample = 0.0, []
-    with threadpool_limits(limits=1):
-        for f, x16 in layers:
-            M = f["M"]
-            n = min(M, max(64, 1024 // len(layers)))
-            rows = np.sort(rng.choice(M, size=n, replace=False))
+    for f, x16 in layers:
+        M = f["M"]
+        n = max(1, int(round(M * row_frac)))
+        rows = np.sort(rng.choice(M, size=n, replace=False))
+        chunk = max(1, (1 << 28) // (8 * f["K"]))
+
+        def once():
+            for r0 in range(0, n, chunk):
+                gemv.gemv_rows(f, x16, rows[r0:r0 + chunk], scale=False)
+        once()
+        ts = []
+        for _ in range(runs):
             t0 = time.perf_counter()
-            gemv.gemv_rows(f, x16, rows)
-            one = time.perf_counter() - t0
-            reps = max(1, min(20, int(budget / max(one, 1e-3))))
-            ts = []
-            for _ in range(reps):
-                t0 = time.perf_counter()
-                gemv.gemv_rows(f, x16, rows)
-                ts.append(time.perf_counter() - t0)
-            t_step += float(np.median(ts)) * M / n
-            sample.append(f"{n}/{M} rows x{reps}")
+            once()
+            ts.append(time.perf_counter() - t0)
+        t_step += float(np.median(ts)) * M / n
+        sample.append(f"{n}/{M} rows")
     return {
         "value": alg_bytes / t_step / 1e9,
         "unit": "GB/s",
         "us_per_step": t_step * 1e6,
-        "cores": 1,
+        "cores": host["blas_threads"],
         "kind": "oracle",
-        "sample": f"random rows (seed 7) per layer: {', '.join(sample)}; median run after 1 warm-up, scaled to "
-                  f"all rows; fp64 numpy, 1 thread; host CPU: {platform.processor() or platform.machine()}",
+        "sample": f"seeded random rows per layer ({', '.join(sample)}), decode + y in fp64 numpy; median of "
+                  f"{runs} runs after 1 warm-up, scaled to all rows. BLAS products on {host['blas_threads']} "
+                  f"threads; the unpack and decode steps are single-threaded numpy",
+        "host": host,
     }
 
 
 def time_graph(torch, launch, steps, warmup, stream, use_graph=True):
-    """Mean ms per launch of `launch(i)` over `steps` launches (one graph replay), HIP events on `stream`."""
+    """Mean ms per launch over `steps` launches, HIP events recorded on `stream`.
+
+    launch(i) must read weight copy i mod copies.  Warm-up: `warmup` eager
+    launches and one replay of a graph of launches 0 .. steps-1.  The timed
+    region replays a second graph of launches steps .. 2*steps-1, so with at
+    least 2*steps copies it reads only copies the warm-up has not touched,
+    and with fewer it cycles through all of them (>= 1 GiB between two reads
+    of one copy): either way the weights come from HBM, not from the 256 MB
+    last-level cache.
+    """
     with torch.cuda.stream(stream):
         for i in range(warmup):
-            launch(i)
+            launch(i % steps)
     torch.cuda.synchronize()
-    graph = None
     if use_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
+        graphs = []
+        for base in (0, steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    launch(base + i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        graphs[0].replay()  # warm-up replay (untimed)
+        torch.cuda.synchronize()
+    else:
+        with torch.cuda.stream(stream):
             for i in range(steps):
                 launch(i)
-        torch.cuda.synchronize()
-        graph.replay()  # warm the graph once (untimed)
         torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         start.record(stream)
-        if graph is not None:
-            graph.replay()
+        if use_graph:
+            graphs[1].replay()
         else:
             for i in range(steps):
-                launch(i)
+                launch(steps + i)
         end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, use_graph):
+    """Per-layer timing of one workload; returns (per_layer, alg_total, ms_total, cpu_layers)."""
+    import numpy as np
+
+    from synth import make_x
+    per_layer, cpu_layers = [], []
+    alg_total, ms_total = 0, 0.0
+    for layer, lname in workload_layers(workload):
+        f = format_inputs(workload, layer)
+        M, K = f["M"], f["K"]
+        host_blob = qgemv.repack(f)
+        # distinct copies whose total is >= rotate_gib; launch i reads copy i % copies
+        copies = max(1, min(512, math.ceil(rotate_gib * (1 << 30) / host_blob.size)))
+        plans = [qgemv.QGemv(f, device="cuda:0", blob=host_blob) for _ in range(copies)]
+        x16 = make_x(workload, B, K, layer, M)
+        x = torch.from_numpy(x16).to(dev)
+        ys = [torch.empty((B, M), dtype=torch.float32, device=dev) for _ in range(copies)]
+        torch.cuda.synchronize()
+
+        def launch(i):
+            plans[i % copies].run(x, ys[i % copies], stream=stream)
+
+        ms = time_graph(torch, launch, steps, warmup, stream, use_graph=use_graph)
+        # every copy that ran must have produced the same, finite y
+        y0 = ys[0].cpu().numpy()
+        assert np.all(np.isfinite(y0)), f"{lname}: non-finite output"
+        for y in ys[1:min(copies, 2 * steps)]:
+            assert np.array_equal(y.cpu().numpy(), y0), f"{lname}: copies disagree"
+        alg = algorithmic_bytes(f, B)
+        alg_total += alg
+        ms_total += ms
+        per_layer.append({"layer": lname, "M": M, "K": K, "nnz": int(f["row_ptr"][-1]), "us": round(ms * 1e3, 3),
+                          "GBs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg,
+                          "weight_copies_rotated": copies,
+                          "distinct_blob_bytes_per_replay": int(min(steps, copies) * host_blob.size),
+                          "timed_copies_untouched_by_warmup": copies >= 2 * steps})
+        cpu_layers.append((f, x16))
+        del plans, ys
+        torch.cuda.empty_cache()
+    return per_layer, alg_total, ms_total, cpu_layers
+
+
+def read_floor(torch, qgemv, nbytes, steps, warmup, stream, dev):
+    """µs of one plain streaming read of nbytes (the library's read probe over
+    distinct windows of a 2 GiB buffer, one graph replay)."""
+    w = int(nbytes) // 16 * 16
+    big = torch.full((2 << 30,), 7, dtype=torch.uint8, device=dev)
+    nwin = (2 << 30) // w
+    sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+    ms = time_graph(torch, lambda i: qgemv.read_probe(big[(i % nwin) * w:(i % nwin + 1) * w], sink, stream=stream),
+                    steps, warmup, stream)
+    del big, sink
+    torch.cuda.empty_cache()
+    return ms * 1e3
+
+
+def summarize_trace(path: str, steps: int, warmup: int) -> str:
+    """Per-launch durations of the timed replays in a rocprofv3 kernel trace.
+
+    For each layer bench.py dispatches the layer's kernel `warmup` times
+    eagerly, then replays two graphs of `steps` launches each (warm-up, then
+    timed); graph capture and the checks between layers dispatch other
+    kernels.  So a run of 2*steps (or warmup + 2*steps) consecutive dispatches
+    of one of the path's kernels ends with a timed replay: its last `steps`
+    dispatches.  Prints median, p10, p90 and mean per timed replay, in µs.
+    """
+    import csv
+
+    import numpy as np
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    ours = lambda n: any(k in n for k in ("k_pair", "k_stream", "k_xlds", "k_huff"))
+    runs = []
+    for t0, t1, name in rows:
+        if runs and runs[-1][0] == name:
+            runs[-1][1].append(t1 - t0)
+        else:
+            runs.append((name, [t1 - t0]))
+    out = [f"timed replays in {os.path.basename(path)} ({steps} launches each, after {warmup} eager warm-up "
+           f"launches and one warm-up replay; durations in us)",
+           "kernel | launches | median | p10 | p90 | mean"]
+    for name, d in runs:
+        if not ours(name) or len(d) not in (2 * steps, warmup + 2 * steps):
+            continue
+        t = np.asarray(d[-steps:], dtype=np.float64) / 1e3
+        short = name.split("(unsigned")[0].replace("void ", "").replace("(anonymous namespace)::", "")
+        out.append(f"{short} | {len(t)} | {np.median(t):.3f} | {np.percentile(t, 10):.3f} | "
+                   f"{np.percentile(t, 90):.3f} | {t.mean():.3f}")
+    return "\n".join(out)
+
+
+TARGETS = ("mlp70b_lut4", "mlp7b_lut3")  # the two batch-1 shapes with a 70 % of 8 TB/s target
 
 
 def main():
@@ -193,21 +345,26 @@ def main():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="skip the second target shape and the per-shape read floors")
     ap.add_argument("--copy-mb", type=int, default=0, help="also time a plain device copy of this many MiB")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured streaming-read ceiling")
     ap.add_argument("--read-probe-mb", type=float, default=0.0,
                     help="only time the read probe over windows of this many MB (rotated through 2 GiB)")
+    ap.add_argument("--trace-summary", default=None, metavar="CSV",
+                    help="only summarise the timed replays of a rocprofv3 kernel_trace.csv (no GPU)")
     a = ap.parse_args()
 
+    if a.trace_summary is not None:
+        print(summarize_trace(a.trace_summary, a.steps, a.warmup))
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from dense_sparse_bit_amd import qgemv
-    from synth import make_x
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     dev = torch.device("cuda:0")
@@ -216,50 +373,14 @@ def main():
     stream = torch.cuda.Stream(device=dev)
 
     if a.read_probe_mb:
-        # Plain streaming reads of one layer's size: distinct windows of a
-        # 2 GiB buffer, so every launch reads from HBM, one HIP-graph replay.
+        us = read_floor(torch, qgemv, a.read_probe_mb * 1e6, a.steps, a.warmup, stream, dev)
         w = int(a.read_probe_mb * 1e6) // 16 * 16
-        big = torch.full((2 << 30,), 7, dtype=torch.uint8, device=dev)
-        nwin = (2 << 30) // w
-        sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
-        ms_p = time_graph(torch, lambda i: qgemv.read_probe(big[(i % nwin) * w:(i % nwin + 1) * w], sink,
-                                                             stream=stream), a.steps, a.warmup, stream)
-        print(json.dumps({"read_probe": {"bytes": w, "us": round(ms_p * 1e3, 3),
-                                         "GBs": round(w / (ms_p * 1e-3) / 1e9, 1), "windows": nwin}}), flush=True)
+        print(json.dumps({"read_probe": {"bytes": w, "us": round(us, 3), "GBs": round(w / (us * 1e-6) / 1e9, 1)}}),
+              flush=True)
         return
 
-    per_layer, cpu_layers = [], []
-    alg_total, ms_total = 0, 0.0
-    for layer, lname in workload_layers(a.workload):
-        f = format_inputs(a.workload, layer)
-        M, K = f["M"], f["K"]
-        host_blob = qgemv.repack(f)
-        copies = max(1, min(a.steps, 256, math.ceil(a.rotate_gib * (1 << 30) / host_blob.size)))
-        plans = [qgemv.QGemv(f, device="cuda:0", blob=host_blob) for _ in range(copies)]
-        x16 = make_x(a.workload, B, K, layer, M)
-        x = torch.from_numpy(x16).to(dev)
-        ys = [torch.empty((B, M), dtype=torch.float32, device=dev) for _ in range(copies)]
-        torch.cuda.synchronize()
-
-        def launch(i):
-            plans[i % copies].run(x, ys[i % copies], stream=stream)
-
-        ms = time_graph(torch, launch, a.steps, a.warmup, stream, use_graph=not a.no_graph)
-        # every copy must have produced the same, finite y
-        y0 = ys[0].cpu().numpy()
-        assert np.all(np.isfinite(y0)), f"{lname}: non-finite output"
-        for y in ys[1:]:
-            assert np.array_equal(y.cpu().numpy(), y0), f"{lname}: copies disagree"
-        alg = algorithmic_bytes(f, B)
-        alg_total += alg
-        ms_total += ms
-        per_layer.append({"layer": lname, "M": M, "K": K, "nnz": int(f["row_ptr"][-1]), "us": round(ms * 1e3, 3),
-                          "GBs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg,
-                          "weight_copies_rotated": copies})
-        cpu_layers.append((f, x16))
-        del plans, ys
-        torch.cuda.empty_cache()
-
+    per_layer, alg_total, ms_total, cpu_layers = measure(torch, qgemv, a.workload, B, a.steps, a.warmup,
+                                                         a.rotate_gib, stream, dev, not a.no_graph)
     us = ms_total * 1e3
     gbs = alg_total / (ms_total * 1e-3) / 1e9
     flops = sum(2.0 * B * p["M"] * p["K"] for p in per_layer)
@@ -284,7 +405,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{a.workload}: {WORKLOAD_NOTES[a.workload]}, batch {B}", "batch": B,
                    "bits": first.get("bits", 0), "format": first["fmt"], "layers": per_layer,
-                   "timing": "eager launches" if a.no_graph else "one HIP-graph replay of all steps per layer"},
+                   "timing": ("eager launches" if a.no_graph else "one HIP-graph replay of all steps per layer") +
+                             ", HIP events on the launch stream; the timed replay reads weight copies the "
+                             "warm-up did not touch (or cycles through >= 1 GiB of them)"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_step": alg_total, "kernel_src_sha": src},
@@ -294,6 +417,23 @@ def main():
         out["mfma"] = {"tflops": round(tf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
                        "util": round(tf / MFMA_F16_PEAK_TFLOPS, 5),
                        "note": "dense flops 2*B*M*K at fp16 MFMA peak; the path stays HBM-bound"}
+    if not a.no_targets and B == 1 and a.workload in TARGETS:
+        # both 70 %-target shapes at batch 1, each next to a plain read of its bytes
+        targets = []
+        for wname in TARGETS:
+            if wname == a.workload:
+                t_us, t_alg = us, alg_total
+            else:
+                pl, t_alg, t_ms, _ = measure(torch, qgemv, wname, 1, a.steps, a.warmup, a.rotate_gib, stream, dev,
+                                             not a.no_graph)
+                t_us = t_ms * 1e3
+            floor_us = read_floor(torch, qgemv, t_alg, a.steps, a.warmup, stream, dev)
+            targets.append({"workload": wname, "us": round(t_us, 3), "GBs": round(t_alg / (t_us * 1e-6) / 1e9, 1),
+                            "frac_of_8TBs": round(t_alg / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "target_us_at_70pct": round(t_alg / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6, 3),
+                            "plain_read_us_same_bytes": round(floor_us, 3),
+                            "frac_of_plain_read": round(floor_us / t_us, 4)})
+        out["targets"] = targets
     if not a.no_ceiling:
         # The streaming-read rate of this GPU, measured in the same run: the
         # library's read probe (16-byte non-temporal loads) over 1 GiB.

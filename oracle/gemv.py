@@ -83,10 +83,11 @@ def sparse_rows(enc: dict, rows) -> tuple:
     return np.concatenate(loc), np.concatenate(col), np.concatenate(val)
 
 
-def gemv_rows(enc: dict, X16: np.ndarray, rows=None, D: np.ndarray | None = None):
+def gemv_rows(enc: dict, X16: np.ndarray, rows=None, D: np.ndarray | None = None, scale: bool = True):
     """y and its tolerance scale A for the selected output rows.
 
-    X16: activations [B, K] (FP16).  Returns (y [B, len(rows)], A [B, len(rows)]) in fp64.
+    X16: activations [B, K] (FP16).  Returns (y [B, len(rows)], A [B, len(rows)]) in fp64;
+    A is None when scale is False (y only).
     """
     M = enc["M"]
     rows = np.arange(M) if rows is None else np.asarray(rows)
@@ -100,7 +101,7 @@ def gemv_rows(enc: dict, X16: np.ndarray, rows=None, D: np.ndarray | None = None
     contrib = val[None, :] * x[:, col]            # [B, nnz_sel]
     for b in range(x.shape[0]):
         np.add.at(y[b], loc, contrib[b])
-    return y, tolerance_scale(x, D, loc, col, val)
+    return y, (tolerance_scale(x, D, loc, col, val) if scale else None)
 
 
 def tolerance_scale(x: np.ndarray, D: np.ndarray, loc, col, val) -> np.ndarray:
