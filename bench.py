@@ -260,6 +260,12 @@ def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, u
         def launch(i):
             plans[i % copies].run(x, ys[i % copies], stream=stream)
 
+        # every copy runs once eagerly before capture (a plan's first batched
+        # run allocates its workspace, which cannot happen under capture)
+        with torch.cuda.stream(stream):
+            for i in range(copies):
+                launch(i)
+        torch.cuda.synchronize()
         ms = time_graph(torch, launch, steps, warmup, stream, use_graph=use_graph)
         # every copy that ran must have produced the same, finite y
         y0 = ys[0].cpu().numpy()

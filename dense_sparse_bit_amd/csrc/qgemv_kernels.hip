@@ -29,6 +29,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/qgemv.h"
@@ -42,6 +43,10 @@ using namespace qgemv_dev;
 struct qgemv_plan {
   BlobHeader h;
   const uint8_t* blob;
+  int device;             // the device of the blob (current at create)
+  void* ws = nullptr;     // workspace of the K-split batched kernel, allocated by the first batched run
+  size_t ws_bytes = 0;
+  std::mutex ws_mu;
 };
 
 namespace {
@@ -1071,6 +1076,331 @@ k_xlds(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, con
 }
 
 // ---------------------------------------------------------------------------
+// Batch 8 / 16 with K split across workgroups.
+//
+// At batch 8 and 16 one K-block of x (NB x 128 FP16: 2 or 4 KiB) outweighs
+// the codes of a (tile, K-block) (768 B or 1 KiB), so a workgroup that owns
+// whole tiles pulls all of x through its CU for only a few tiles.  Here
+// workgroup b owns the tiles of group b % NG and the K-blocks [kb0, kb1) of
+// split b / NG (S splits of the K-blocks): it copies its x slice once into LDS
+// ([pieces of 8 columns][NB][8] FP16, one MFMA B-operand piece per 16 bytes)
+// and uses it for all of its tiles.  Block indices go round-robin over the
+// eight XCDs, so with NG a multiple of 8 the S workgroups of a group (block
+// indices gi + NG s) run on one XCD.
+//
+// Inside the workgroup the waves take chunks of CH K-blocks of one tile in
+// order from an LDS counter, as in k_stream, and each chunk writes its own
+// partial slot.  The outliers of each (tile, K-block) go through the MFMAs
+// with the block, as in k_stream: loaded from the block-grouped copy next to
+// the codes, scattered into the wave's zeroed 16x128 FP16 tile in LDS, read
+// back as four A operands and multiplied with the block's x.  Each output of
+// the group then adds its tile's chunks in order.  The S splits meet in the
+// workspace: each writes its [rows][NB] partial, and the last to arrive (a
+// counter per group) adds the S partials in split order and writes y, so the
+// result does not depend on timing.  Each arrival adds 8 / S to the counter,
+// so the counter is a multiple of 8 between launches whatever plans used it,
+// and the arrival that reaches the next multiple is the last: nothing needs
+// clearing.
+// ---------------------------------------------------------------------------
+template <int FMT, int BITS, int NB, int CH>
+__global__ void __launch_bounds__(64 * kWaves)
+k_split(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, const int32_t* __restrict__ boff,
+        const uint32_t* __restrict__ bent, const uint16_t* __restrict__ x, float* __restrict__ y,
+        float* __restrict__ wpart, uint32_t* __restrict__ wctr, int M, int K, int nkb, int tiles,
+        uint32_t codes_bytes, uint32_t meta_bytes, int nnz, int gsz, int S, int NG) {
+  using F = Fmt<FMT, BITS>;
+  constexpr int BB = 256 * BITS;
+  extern __shared__ uint32_t lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gi = (int)(blockIdx.x % (unsigned)NG), si = (int)(blockIdx.x / (unsigned)NG);
+  const int T0 = (int)((int64_t)gi * tiles / NG), T1 = (int)((int64_t)(gi + 1) * tiles / NG);
+  const int TW = T1 - T0;
+  const int kb0 = si * nkb / S, kb1 = (si + 1) * nkb / S, KB = kb1 - kb0;
+  const int CPT = (KB + CH - 1) / CH;  // chunks per tile
+  const int nchunks = TW * CPT;
+  const int nrows = min(TW * 16, M - T0 * 16);
+  const int OB = (KB + 4) & ~3;  // block outlier offsets staged per tile (KB + 1, padded)
+
+  // LDS: xs [KB*16][NB][8] FP16 | part [nchunks][16][NB] | offsets [TW][OB] | counter, flag (4 ints)
+  //      | LUT [TW*16][tab_dw] | outlier tiles [16 waves][16][128] FP16
+  uint16_t* xs = (uint16_t*)lds;
+  float* part = (float*)(lds + KB * 64 * NB);
+  int* bo_lds = (int*)(part + nchunks * 16 * NB);
+  int* chunk_ctr = bo_lds + TW * OB;
+  int* last_flag = chunk_ctr + 1;
+  uint32_t* lut_lds = (uint32_t*)(chunk_ctr + 4);  // 16-byte aligned
+  uint16_t* otile = (uint16_t*)(lut_lds + (F::lut ? TW * 16 * F::tab_dw : 0)) + 2048 * w;
+
+  const rsrc_t rc = make_rsrc(codes, codes_bytes);
+  const rsrc_t rs = make_rsrc(meta, F::lut ? 0u : meta_bytes);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)NB * (uint32_t)K * 2u);
+  const rsrc_t rbo = make_rsrc(boff, (uint32_t)((uint64_t)tiles * nkb + 1) * 4);
+  const rsrc_t rbe = make_rsrc(bent, (uint32_t)nnz * 4);
+
+  // Prologue: the block outlier offsets and the tables, then the x slice
+  // straight into LDS; all of it lands before the code ring is issued.
+  int bo[2] = {0, 0};  // offsets of (local tile, block) pairs tid and tid + 1024
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = (int)threadIdx.x + 1024 * k, t = i / OB, j = i - t * OB;
+    bo[k] = __builtin_amdgcn_raw_buffer_load_b32(
+        rbo, t < TW && j <= KB ? ((T0 + t) * nkb + kb0 + j) * 4 : (int)kOutOfRange, 0, 0);
+  }
+  u32x4_t ls = {0u, 0u, 0u, 0u};
+  const int lpieces = F::lut ? TW * 16 * F::tab_dw / 4 : 0;
+  if constexpr (F::lut) {
+    const rsrc_t rl = make_rsrc(meta, meta_bytes);
+    ls = __builtin_amdgcn_raw_buffer_load_b128(
+        rl, (int)threadIdx.x < lpieces ? (T0 * 16 * F::tab_dw / 4 + (int)threadIdx.x) * 16 : (int)kOutOfRange, 0,
+        kNonTemporal);
+  }
+  const int xpieces = KB * 16 * NB;  // a multiple of 64
+  for (int i = w; 64 * i < xpieces; i += kWaves) {
+    const int piece = 64 * i + lane;
+    const int j = piece / NB, n = piece % NB;
+    const int col = kb0 * kBlockK + 8 * j;
+    const int off = col < K ? (n * K + col) * 2 : (int)kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xs + 512 * i), 16, off, 0,
+                                             0, 0);
+  }
+
+  const uint32_t voff = (uint32_t)lane * 4 * BITS;
+  const uint32_t zoff = (uint32_t)(lane & 15) * 16 + (uint32_t)(lane >> 4) * 4;
+  const uint32_t spoff = 256 + (uint32_t)(lane >> 4) * 64 + (uint32_t)(lane & 15) * 4;
+  const uint32_t cunit = 16384u / (uint32_t)gsz;  // BPDQ coefficients, as in k_stream
+  const uint32_t coff =
+      ((uint32_t)(lane & 15) * (128u / (uint32_t)gsz) + (uint32_t)(32 * (lane >> 4)) / (uint32_t)gsz) * 8u;
+  uint32_t cb[CH][BITS];
+  uint32_t sb[CH][2];
+  uint32_t ent[CH];  // the block's outliers, one per lane (up to 64; more are read at decode)
+  int elo[CH], ecnt[CH];
+  auto issue = [&](int u, int g) {  // g: blob block index, -1 for none
+    const bool in = g >= 0;
+    load_chunk<BITS>(cb[u], rc, in ? (uint32_t)g * BB + voff : kOutOfRange);
+    if constexpr (F::bpdq) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(in ? (uint32_t)g * cunit + coff : kOutOfRange),
+                                                             0, kNonTemporal);
+      sb[u][0] = v[0];
+      sb[u][1] = v[1];
+    } else if constexpr (!F::lut) {
+      sb[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? (uint32_t)g * 512 + zoff : kOutOfRange), 0,
+                                                      kNonTemporal);
+      sb[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(in ? (uint32_t)g * 512 + spoff : kOutOfRange), 0,
+                                                      kNonTemporal);
+    } else {
+      sb[u][0] = sb[u][1] = 0;
+    }
+  };
+  auto issue_ent = [&](int u, int lo, int n) {
+    ent[u] = __builtin_amdgcn_raw_buffer_load_b32(rbe, lane < n ? (lo + lane) * 4 : (int)kOutOfRange, 0, kNonTemporal);
+    elo[u] = lo;
+    ecnt[u] = n;
+  };
+  // Chunk q: local tile q / CPT, K-blocks kb .. kb + nv - 1 of the split,
+  // blob block g0 of the first, staged offsets at bo_lds[t * OB + kb - kb0].
+  struct Chunk {
+    int q, t, kb, g0, nv;
+  };
+  auto chunk_at = [&](int q) -> Chunk {
+    Chunk k;
+    k.q = q;
+    k.t = q / CPT;
+    k.kb = kb0 + (q - k.t * CPT) * CH;
+    k.g0 = (T0 + k.t) * nkb + k.kb;
+    k.nv = q < nchunks ? min(CH, kb1 - k.kb) : 0;
+    return k;
+  };
+  // the outlier offsets of a chunk's blocks (lane i: block i's start, i <= nv)
+  auto chunk_offsets = [&](const Chunk& k) {
+    return lane <= k.nv && k.nv > 0 ? bo_lds[k.t * OB + k.kb - kb0 + lane] : 0;
+  };
+  // The first chunk's loads go out behind the staged ones; the wait below
+  // covers the staged loads alone (they were issued first and complete in
+  // order), so the ring runs on across the barrier.
+  Chunk ck = chunk_at(w);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < CH; ++u) issue(u, u < ck.nv ? ck.g0 + u : -1);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kRing = CH * (F::lut ? 1 : F::bpdq ? 2 : 3);  // vector loads per ring fill
+  static_assert(kRing < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kRing & 15) | ((kRing >> 4) << 14));
+
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = (int)threadIdx.x + 1024 * k;
+    if (i < TW * OB) bo_lds[i] = bo[k];
+  }
+  if constexpr (F::lut) {
+    if ((int)threadIdx.x < lpieces) ((u32x4_t*)lut_lds)[threadIdx.x] = ls;
+  }
+  {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ((u32x4_t*)otile)[lane + 64 * k] = z;
+  }
+  if (threadIdx.x == 0) *chunk_ctr = kWaves;
+  lds_barrier();
+  {
+    const int obv = chunk_offsets(ck);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int lo = __builtin_amdgcn_readlane(obv, u);
+      issue_ent(u, lo, u < ck.nv ? __builtin_amdgcn_readlane(obv, u + 1) - lo : 0);
+    }
+  }
+  auto next_chunk = [&]() -> Chunk {
+    int q = 0;
+    if (lane == 0) q = lds_fetch_add(chunk_ctr, 1);
+    return chunk_at(__builtin_amdgcn_readfirstlane(q));
+  };
+
+  int tc = -1;  // local tile whose table is in tab
+  uint32_t tab[F::tab_dw];
+  auto planes = [&]() {
+    if constexpr (F::lut) {
+      const uint32_t* L = lut_lds + (tc * 16 + (lane & 15)) * F::tab_dw;
+      uint32_t Lr[F::tab_dw];
+#pragma unroll
+      for (int i = 0; i < F::tab_dw; ++i) Lr[i] = L[i];
+      if constexpr (BITS == 4) l4_planes(Lr, tab);
+      else l3_planes(Lr, tab);
+    } else {
+      tab[0] = 0;
+    }
+  };
+  // B operand of lane (n, q) = (lane % 16, lane / 16), step s2 of K-block kb:
+  // x[n][128 kb + 32 q + 8 s2 .. +7], piece 16 (kb - kb0) + 4 q + s2 of the slice.
+  const uint16_t* xb = xs + (4 * (lane >> 4) * NB + ((lane & 15) & (NB - 1))) * 8;
+  while (ck.q < nchunks) {
+    const Chunk nx = next_chunk();
+    const int obv = chunk_offsets(nx);
+    if (ck.t != tc) {
+      tc = ck.t;
+      planes();
+    }
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (u < ck.nv) {
+        uint32_t am[F::n_mfma][4];
+        if constexpr (F::lut || F::bpdq) {
+          decode_chunk<FMT, BITS>(cb[u], sb[u], tab, am);
+        } else {
+          const uint32_t st[2] = {perm(sb[u][0], sb[u][1], 0x05040100u), perm(sb[u][0], sb[u][1], 0x07060302u)};
+          decode_chunk<FMT, BITS>(cb[u], st, tab, am);
+        }
+        const int kbl = ck.kb + u - kb0;
+        half8_t bx[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          bx[s2] = *(const half8_t*)(xb + (16 * kbl + s2) * NB * 8);
+          acc = mfma(h8(am[s2][0], am[s2][1], am[s2][2], am[s2][3]), bx[s2], acc);
+          if constexpr (!F::lut)
+            acc = mfma(h8(am[4 + s2][0], am[4 + s2][1], am[4 + s2][2], am[4 + s2][3]), bx[s2], acc);
+        }
+        // The block's outliers: scattered into the wave's zero 16x128 tile
+        // in A-operand order, multiplied with the block's x like the dense
+        // codes, then cleared.
+        const int n = ecnt[u];
+        if (n > 0) {
+          auto place = [&](uint32_t e) {
+            const uint32_t c = e & 127u, m = (e >> 7) & 15u;
+            return (((c >> 3) & 3u) * 64u + m + 16u * (c >> 5)) * 8u + (c & 7u);
+          };
+          uint32_t oa = 0;
+          if (lane < n) {
+            oa = place(ent[u]);
+            otile[oa] = (uint16_t)(ent[u] >> 16);
+          }
+          for (int p = 64; p < n; p += 64)  // more than 64 in the block
+            if (lane + p < n) {
+              const uint32_t e = bent[elo[u] + p + lane];
+              otile[place(e)] = (uint16_t)(e >> 16);
+            }
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const u32x4_t av = ((const u32x4_t*)otile)[s2 * 64 + lane];
+            acc = mfma(h8(av[0], av[1], av[2], av[3]), bx[s2], acc);
+          }
+          if (n <= 64) {
+            if (lane < n) otile[oa] = 0;
+          } else {
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ((u32x4_t*)otile)[lane + 64 * k] = z;
+          }
+        }
+      }
+      issue(u, u < nx.nv ? nx.g0 + u : -1);
+      const int lo = __builtin_amdgcn_readlane(obv, u);
+      issue_ent(u, lo, u < nx.nv ? __builtin_amdgcn_readlane(obv, u + 1) - lo : 0);
+    }
+    // acc[i]: row 4*(lane/16) + i of the chunk's tile, batch column lane % 16
+    float* sl = part + ck.q * 16 * NB;
+    if ((lane & 15) < NB)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sl[(4 * (lane >> 4) + i) * NB + (lane & 15)] = acc[i];
+    ck = nx;
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+
+  // Each output (row r, batch column n) adds its tile's chunk partials in
+  // chunk order; a thread takes four batch columns of one row (16 bytes).
+  const bool split = S > 1;
+  constexpr int kSc1 = 16;  // cache policy: device-coherent (bypass the XCD's non-coherent L2 copy)
+  const rsrc_t rw = make_rsrc(wpart, (uint32_t)((uint64_t)S * tiles * 16 * NB * 4));
+  const uint32_t wbase = (uint32_t)((si * tiles + T0) * 16 * NB) * 4u;  // this split's partials of the group
+  for (int i = threadIdx.x; i < nrows * NB / 4; i += 64 * kWaves) {
+    const int r = i / (NB / 4), n4 = 4 * (i - r * (NB / 4));
+    const float* ps = part + (r >> 4) * CPT * 16 * NB + (r & 15) * NB + n4;
+    floatx4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < CPT; ++j) v += *(const floatx4_t*)(ps + j * 16 * NB);
+    if (split) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rw, (int)(wbase + 16u * (uint32_t)i), 0,
+                                             kSc1);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[(size_t)(n4 + k) * M + T0 * 16 + r] = v[k];
+    }
+  }
+  if (!split) return;
+
+  // The splits meet.  The partials went out as device-coherent stores; each
+  // thread waits until its stores are acknowledged, and after the barrier
+  // one thread counts the workgroup's arrival.  The last of the S reads the S
+  // partials with device-coherent loads, after its count returned, and adds
+  // them in split order.  No L2 write-back or invalidate is needed.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t add = 8u / (uint32_t)S;
+    const uint32_t old = __hip_atomic_fetch_add(wctr + gi, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last_flag = ((old + add) & 7u) == 0u;
+  }
+  __syncthreads();
+  if (!*last_flag) return;
+  for (int i = threadIdx.x; i < nrows * NB / 4; i += 64 * kWaves) {
+    const int r = i / (NB / 4), n4 = 4 * (i - r * (NB / 4));
+    u32x4_t pv[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      pv[s2] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, s2 < S ? (int)((uint32_t)((s2 * tiles + T0) * 16 * NB) * 4u + 16u * (uint32_t)i) : (int)kOutOfRange, 0,
+          kSc1);
+    floatx4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      if (s2 < S) v += __builtin_bit_cast(floatx4_t, pv[s2]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[(size_t)(n4 + k) * M + T0 * 16 + r] = v[k];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Batch 1, 4-bit LUT codes: pair tables in LDS.
 //
 // A byte of an L4 chunk holds two codes, A (chunk column k) and B (column
@@ -1829,6 +2159,82 @@ hipError_t launch_pair(const qgemv_plan* p, const uint16_t* x, float* y, hipStre
   return hipGetLastError();
 }
 
+// K-split batched kernel.  S splits of the K-blocks times NG tile groups
+// (NG a multiple of 8 when it can be, so that a group's splits share an
+// XCD), chunks of CH K-blocks.  LDS: x slice, chunk partials, staged block
+// outlier offsets, counters, tables, and the 16 waves' 4 KiB outlier tiles.
+struct SplitCfg {
+  int S, NG, CH;
+  size_t lds;
+};
+
+size_t split_lds(const BlobHeader& h, int nb, int S, int NG, int CH) {
+  const size_t tw = (size_t)((h.tiles + NG - 1) / NG);
+  const size_t kbm = (size_t)((h.nkb + S - 1) / S);
+  const size_t cpt = (kbm + CH - 1) / CH;
+  const size_t ob = (kbm + 4) & ~(size_t)3;
+  const size_t tab = h.format == QGEMV_FMT_LUT ? (size_t)(2u << h.bits) : 0;  // table bytes per row
+  return kbm * 256 * nb + tw * cpt * 16 * nb * 4 + tw * ob * 4 + 16 + tw * 16 * tab + (size_t)kWaves * 4096;
+}
+
+// The first (S, CH) in order of preference that fits: S = 4 keeps a quarter
+// of x per CU with one read-back per group of four; S = 8 for long K; larger
+// chunks when the chunk partials would not fit.  The staged offsets of a
+// workgroup must fit two per thread.
+bool split_config(const BlobHeader& h, int nb, SplitCfg& c) {
+  // Uniform codes only: LUT and BPDQ decodes are bound by the VALU, not by x.
+  if (h.format != QGEMV_FMT_UNIFORM) return false;
+  for (int S : {4, 8, 2}) {
+    if (S > h.nkb) continue;
+    int NG = h.tiles < kMaxGrid / S ? h.tiles : kMaxGrid / S;
+    if (NG >= 8) NG &= ~7;
+    const int tw = (h.tiles + NG - 1) / NG, kbm = (h.nkb + S - 1) / S;
+    if (tw * ((kbm + 4) & ~3) > 2 * 64 * kWaves) continue;
+    for (int CH : {2, 4, 8}) {
+      const size_t lds = split_lds(h, nb, S, NG, CH);
+      if (lds > kLdsBytes) continue;
+      c.S = S;
+      c.NG = NG;
+      c.CH = CH;
+      c.lds = lds < kOneWorkgroupLds ? kOneWorkgroupLds : lds;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Workspace of the K-split kernel: 1 KiB of counters (one per tile group),
+// then the partials [S][tiles * 16][nb] fp32.
+constexpr size_t kSplitCtrBytes = 1024;
+size_t split_ws_bytes(const BlobHeader& h, int nb, const SplitCfg& c) {
+  return kSplitCtrBytes + (size_t)c.S * h.tiles * 16 * nb * 4;
+}
+
+template <int FMT, int BITS, int NB, int CH>
+hipError_t launch_split_ch(const qgemv_plan* p, const SplitCfg& c, const uint16_t* x, float* y, void* ws,
+                           hipStream_t st) {
+  const BlobHeader& h = p->h;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_split<FMT, BITS, NB, CH>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const uint32_t codes_bytes = (uint32_t)((uint64_t)h.tiles * h.nkb * h.block_bytes);
+  const uint32_t meta_bytes = (uint32_t)(h.off_rowptr - h.off_meta);
+  hipLaunchKernelGGL((k_split<FMT, BITS, NB, CH>), dim3(c.NG * c.S), dim3(64 * kWaves), c.lds, st,
+                     p->blob + h.off_codes, (const uint32_t*)(p->blob + h.off_meta),
+                     (const int32_t*)(p->blob + h.off_boff), (const uint32_t*)(p->blob + h.off_bent), x, y,
+                     (float*)((uint8_t*)ws + kSplitCtrBytes), (uint32_t*)ws, h.M, h.K, h.nkb, h.tiles, codes_bytes,
+                     meta_bytes, (int)h.nnz, h.group_size > 0 ? h.group_size : 16, c.S, c.NG);
+  return hipGetLastError();
+}
+
+template <int FMT, int BITS, int NB>
+hipError_t launch_split(const qgemv_plan* p, const SplitCfg& c, const uint16_t* x, float* y, void* ws,
+                        hipStream_t st) {
+  return c.CH == 2   ? launch_split_ch<FMT, BITS, NB, 2>(p, c, x, y, ws, st)
+         : c.CH == 4 ? launch_split_ch<FMT, BITS, NB, 4>(p, c, x, y, ws, st)
+                     : launch_split_ch<FMT, BITS, NB, 8>(p, c, x, y, ws, st);
+}
+
 // HPTQ: one workgroup per CU over its tile range; G = 3 blocks decoded side
 // by side per wave where their buffers fit in LDS and their registers fit
 // without spilling, else fewer.  Long codewords
@@ -1891,12 +2297,17 @@ hipError_t launch_huff(const qgemv_plan* p, const uint16_t* x, float* y, int bat
                       : launch_huff_nb<16>(p, x, y, st);
 }
 
+// ws: the K-split workspace for this batch (split_ws_bytes), or null to use
+// the kernels that need none.
 template <int FMT, int BITS>
-hipError_t launch_run(const qgemv_plan* p, const uint16_t* x, float* y, int batch, hipStream_t st) {
+hipError_t launch_run(const qgemv_plan* p, const uint16_t* x, float* y, int batch, void* ws, hipStream_t st) {
   if (batch == 1) {
     if (FMT == QGEMV_FMT_LUT && BITS == 4 && pair_fits(p->h)) return launch_pair(p, x, y, st);
     return launch_stream<FMT, BITS, 1>(p, x, y, st);
   }
+  SplitCfg c;
+  if (ws && split_config(p->h, batch, c))
+    return batch == 8 ? launch_split<FMT, BITS, 8>(p, c, x, y, ws, st) : launch_split<FMT, BITS, 16>(p, c, x, y, ws, st);
   if (batch == 8)
     return xlds_fits(p->h, 8) ? launch_xlds<FMT, BITS, 8>(p, x, y, st) : launch_stream<FMT, BITS, 8>(p, x, y, st);
   return xlds_fits(p->h, 16) ? launch_xlds<FMT, BITS, 16>(p, x, y, st) : launch_stream<FMT, BITS, 16>(p, x, y, st);
@@ -1944,6 +2355,62 @@ int hip_status(hipError_t e) {
   return QGEMV_ERR_HIP;
 }
 
+// Bytes of K-split workspace a plan's batched runs need (0 if none).
+size_t plan_ws_need(const qgemv_plan* p) {
+  size_t need = 0;
+  for (int nb : {8, 16}) {
+    SplitCfg c;
+    if (split_config(p->h, nb, c)) {
+      const size_t b = split_ws_bytes(p->h, nb, c);
+      if (b > need) need = b;
+    }
+  }
+  return need;
+}
+
+// The plan's workspace, allocated on the plan's device by its first batched
+// run: counters cleared (in stream order, before the first use), partials
+// left as they are (every launch writes the partials it reads).  A run under
+// stream capture cannot allocate it and fails instead.
+int plan_workspace(qgemv_plan* p, hipStream_t st, void** ws) {
+  *ws = nullptr;
+  const size_t need = plan_ws_need(p);
+  if (need == 0) return QGEMV_OK;
+  std::lock_guard<std::mutex> lock(p->ws_mu);
+  if (!p->ws) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return hip_status(e);
+    if (cs != hipStreamCaptureStatusNone) return QGEMV_ERR_INVALID_ARG;
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != p->device && (e = hipSetDevice(p->device)) != hipSuccess) return hip_status(e);
+    void* mem = nullptr;
+    e = hipMalloc(&mem, need);
+    if (e == hipSuccess) e = hipMemsetAsync(mem, 0, kSplitCtrBytes, st);
+    if (cur != p->device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      if (mem) (void)hipFree(mem);
+      return hip_status(e);
+    }
+    p->ws = mem;
+    p->ws_bytes = need;
+  }
+  *ws = p->ws;
+  return QGEMV_OK;
+}
+
+hipError_t launch_format(const qgemv_plan* p, const uint16_t* x, float* y, int batch, void* ws, hipStream_t st) {
+  const bool b4 = p->h.bits == 4;
+  if (p->h.format == QGEMV_FMT_HPTQ) return launch_huff(p, x, y, batch, st);
+  if (p->h.format == QGEMV_FMT_LUT)
+    return b4 ? launch_run<QGEMV_FMT_LUT, 4>(p, x, y, batch, ws, st) : launch_run<QGEMV_FMT_LUT, 3>(p, x, y, batch, ws, st);
+  if (p->h.format == QGEMV_FMT_BPDQ) return launch_run<QGEMV_FMT_BPDQ, 3>(p, x, y, batch, ws, st);
+  return b4 ? launch_run<QGEMV_FMT_UNIFORM, 4>(p, x, y, batch, ws, st)
+            : launch_run<QGEMV_FMT_UNIFORM, 3>(p, x, y, batch, ws, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1969,7 +2436,10 @@ int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* pack
     if (bytes < expect.total_bytes) return QGEMV_ERR_SIZE;
   }
   if (std::memcmp(&got, &expect, sizeof(got)) != 0) return QGEMV_ERR_SIZE;
-  qgemv_plan* p = new (std::nothrow) qgemv_plan{expect, (const uint8_t*)packed_dev};
+  int dev = 0;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return hip_status(de);
+  qgemv_plan* p = new (std::nothrow) qgemv_plan{expect, (const uint8_t*)packed_dev, dev};
   if (!p) return QGEMV_ERR_INVALID_ARG;
   *out = p;
   return QGEMV_OK;
@@ -1980,18 +2450,12 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
   if ((uintptr_t)x_dev % 16 || (uintptr_t)y_dev % 16) return QGEMV_ERR_INVALID_ARG;
   if (batch != 1 && batch != 8 && batch != 16) return QGEMV_ERR_UNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
-  const uint16_t* x = (const uint16_t*)x_dev;
-  const bool b4 = h->h.bits == 4;
-  hipError_t e;
-  if (h->h.format == QGEMV_FMT_HPTQ) return hip_status(launch_huff(h, x, y_dev, batch, st));
-  if (h->h.format == QGEMV_FMT_LUT)
-    e = b4 ? launch_run<QGEMV_FMT_LUT, 4>(h, x, y_dev, batch, st) : launch_run<QGEMV_FMT_LUT, 3>(h, x, y_dev, batch, st);
-  else if (h->h.format == QGEMV_FMT_BPDQ)
-    e = launch_run<QGEMV_FMT_BPDQ, 3>(h, x, y_dev, batch, st);
-  else
-    e = b4 ? launch_run<QGEMV_FMT_UNIFORM, 4>(h, x, y_dev, batch, st)
-           : launch_run<QGEMV_FMT_UNIFORM, 3>(h, x, y_dev, batch, st);
-  return hip_status(e);
+  void* ws = nullptr;
+  if (batch > 1) {
+    const int stw = plan_workspace(h, st, &ws);
+    if (stw != QGEMV_OK) return stw;
+  }
+  return hip_status(launch_format(h, (const uint16_t*)x_dev, y_dev, batch, ws, st));
 }
 
 int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream) {
@@ -2019,6 +2483,7 @@ int qgemv_read_probe(const void* src_dev, uint64_t bytes, uint32_t* sink_dev, in
 }
 
 int qgemv_destroy(qgemv_handle h) {
+  if (h && h->ws) (void)hipFree(h->ws);
   delete h;
   return QGEMV_OK;
 }

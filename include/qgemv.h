@@ -163,8 +163,9 @@ int qgemv_unpack_host(const void* blob_host, size_t bytes, uint8_t* codes_out, s
  * 256-byte aligned).  shape supplies M, K, bits, format, group_size and nnz;
  * its array pointers are ignored.  The blob's header is read back once
  * (synchronous device-to-host copy) and must match shape.  The caller keeps
- * the blob alive and unmodified until qgemv_destroy.  The plan allocates no
- * device memory.
+ * the blob alive and unmodified until qgemv_destroy.  qgemv_create
+ * allocates no device memory (see qgemv_run for the batch-8/16 workspace).
+ * The plan belongs to the device current at this call.
  * Errors: INVALID_ARG, UNSUPPORTED, SIZE (bytes too small or header mismatch),
  * HIP.
  */
@@ -177,8 +178,16 @@ int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* pack
  * aligned; every element is overwritten.  batch must be 1, 8 or 16.
  * Asynchronous: errors of the running kernel surface at the caller's next
  * synchronisation.
- * Errors: INVALID_ARG (null handle/pointer, misalignment), UNSUPPORTED (batch),
- * HIP (launch failure).
+ * Workspace: with uniform codes at batch 8 or 16 the K dimension is split
+ * across workgroups whose partial sums meet in a device workspace of the
+ * plan (S * ceil(M/16) * 16 * 16 * 4 bytes of partials, S <= 8, plus 1 KiB
+ * of counters).  The first such run of a plan allocates it (hipMalloc on the
+ * plan's device, counters cleared in stream order) and must not be captured
+ * into a graph; later runs, captured or not, reuse it.  Runs of one plan at
+ * batch 8/16 that overlap in time (other streams) share it and race.
+ * Errors: INVALID_ARG (null handle/pointer, misalignment, workspace first
+ * needed under stream capture), UNSUPPORTED (batch), HIP (launch or
+ * allocation failure).
  */
 int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, void* stream);
 
@@ -204,7 +213,8 @@ int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream);
  */
 int qgemv_read_probe(const void* src_dev, uint64_t bytes, uint32_t* sink_dev, int32_t sink_words, void* stream);
 
-/* Release the plan (host memory only).  NULL is accepted. */
+/* Release the plan and its workspace, if any (the plan's enqueued work must
+ * have completed).  NULL is accepted. */
 int qgemv_destroy(qgemv_handle h);
 
 /* Static description of a status code; never NULL. */
