@@ -648,6 +648,7 @@ const char* qgemv_error_string(int status) {
     case QGEMV_ERR_UNSUPPORTED: return "unsupported bits/format/group/K/batch";
     case QGEMV_ERR_HIP: return "HIP runtime error";
     case QGEMV_ERR_SIZE: return "buffer too small or blob header mismatch";
+    case QGEMV_ERR_SCRATCH: return "workspace needed exceeds the static scratch of qgemv_run_noalloc";
     default: return "unknown status";
   }
 }

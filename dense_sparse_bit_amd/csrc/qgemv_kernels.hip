@@ -49,6 +49,13 @@ struct qgemv_plan {
   std::mutex ws_mu;
 };
 
+// Workspace of qgemv_run_noalloc, for callers that cannot allocate device
+// memory: one static array per device, zero at load, held until the process
+// ends.  Host code uses only the address hipGetSymbolAddress returns for it
+// on each device (g_scratch_dev), never the array's name.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -2401,6 +2408,32 @@ int plan_workspace(qgemv_plan* p, hipStream_t st, void** ws) {
   return QGEMV_OK;
 }
 
+// Device address of `scratch` on device dev, looked up once per device with
+// that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+int scratch_address(int dev, void** out) {
+  *out = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return QGEMV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (!ptr) return QGEMV_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return QGEMV_OK;
+}
+
 hipError_t launch_format(const qgemv_plan* p, const uint16_t* x, float* y, int batch, void* ws, hipStream_t st) {
   const bool b4 = p->h.bits == 4;
   if (p->h.format == QGEMV_FMT_HPTQ) return launch_huff(p, x, y, batch, st);
@@ -2456,6 +2489,20 @@ int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, vo
     if (stw != QGEMV_OK) return stw;
   }
   return hip_status(launch_format(h, (const uint16_t*)x_dev, y_dev, batch, ws, st));
+}
+
+int qgemv_run_noalloc(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, void* stream) {
+  if (!h || !x_dev || !y_dev) return QGEMV_ERR_INVALID_ARG;
+  if ((uintptr_t)x_dev % 16 || (uintptr_t)y_dev % 16) return QGEMV_ERR_INVALID_ARG;
+  if (batch != 1 && batch != 8 && batch != 16) return QGEMV_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  SplitCfg c;
+  if (batch > 1 && split_config(h->h, batch, c)) {
+    if (split_ws_bytes(h->h, batch, c) > kScratchBytes) return QGEMV_ERR_SCRATCH;
+    const int sts = scratch_address(h->device, &ws);
+    if (sts != QGEMV_OK) return sts;
+  }
+  return hip_status(launch_format(h, (const uint16_t*)x_dev, y_dev, batch, ws, (hipStream_t)stream));
 }
 
 int qgemv_debug_unpack(qgemv_handle h, uint8_t* codes_dev, void* stream) {

@@ -28,7 +28,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qgemv.h")
 
 FMT = {"uniform": 0, "lut": 1, "bpdq": 2, "hptq": 3}
 STATUS = {0: "QGEMV_OK", -1: "QGEMV_ERR_INVALID_ARG", -2: "QGEMV_ERR_MALFORMED_CSR",
-          -3: "QGEMV_ERR_UNSUPPORTED", -4: "QGEMV_ERR_HIP", -5: "QGEMV_ERR_SIZE"}
+          -3: "QGEMV_ERR_UNSUPPORTED", -4: "QGEMV_ERR_HIP", -5: "QGEMV_ERR_SIZE", -6: "QGEMV_ERR_SCRATCH"}
 
 
 
@@ -76,13 +76,15 @@ def lib() -> ctypes.CDLL:
     L.qgemv_unpack_host.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]
     L.qgemv_create.argtypes = [P(ctypes.c_void_p), P(Weights), ctypes.c_void_p, ctypes.c_size_t]
     L.qgemv_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    L.qgemv_run_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.c_void_p]
     L.qgemv_debug_unpack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.qgemv_destroy.argtypes = [ctypes.c_void_p]
     L.qgemv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     L.qgemv_error_string.argtypes = [ctypes.c_int]
     L.qgemv_error_string.restype = ctypes.c_char_p
     L.qgemv_last_hip_error.argtypes = []
-    for f in ("qgemv_packed_size", "qgemv_repack", "qgemv_unpack_host", "qgemv_create", "qgemv_run",
+    for f in ("qgemv_packed_size", "qgemv_repack", "qgemv_unpack_host", "qgemv_create", "qgemv_run", "qgemv_run_noalloc",
               "qgemv_debug_unpack", "qgemv_read_probe", "qgemv_destroy", "qgemv_last_hip_error"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -194,6 +196,20 @@ class QGemv:
             raise ValueError("y must be a contiguous fp32 [B, M] tensor")
         s = (stream or torch.cuda.current_stream(x.device)).cuda_stream
         _check(lib().qgemv_run(self._h, x.data_ptr(), y.data_ptr(), B, s), "qgemv_run")
+        return y
+
+    def run_noalloc(self, x, y, stream=None):
+        """As run(), into a given y, through qgemv_run_noalloc (no device allocation)."""
+        import torch
+        if x.dim() == 1:
+            x = x.unsqueeze(0)
+        if x.dtype != torch.float16 or not x.is_contiguous() or x.shape[1] != self.K:
+            raise ValueError("x must be a contiguous FP16 [B, K] tensor")
+        B = x.shape[0]
+        if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (B, self.M):
+            raise ValueError("y must be a contiguous fp32 [B, M] tensor")
+        s = (stream or torch.cuda.current_stream(x.device)).cuda_stream
+        _check(lib().qgemv_run_noalloc(self._h, x.data_ptr(), y.data_ptr(), B, s), "qgemv_run_noalloc")
         return y
 
     def debug_unpack(self, stream=None):

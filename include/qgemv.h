@@ -53,8 +53,10 @@ typedef enum {
                                    supported set (see qgemv_weights and qgemv_run)      */
   QGEMV_ERR_HIP = -4,           /* a HIP runtime call failed; qgemv_last_hip_error()
                                    returns its hipError_t value                          */
-  QGEMV_ERR_SIZE = -5           /* destination / blob buffer too small, or the blob
+  QGEMV_ERR_SIZE = -5,          /* destination / blob buffer too small, or the blob
                                    header does not match the descriptor                  */
+  QGEMV_ERR_SCRATCH = -6        /* qgemv_run_noalloc: the shape needs more workspace
+                                   than the library's static scratch holds               */
 } qgemv_status;
 
 typedef enum {
@@ -190,6 +192,23 @@ int qgemv_create(qgemv_handle* out, const qgemv_weights* shape, const void* pack
  * allocation failure).
  */
 int qgemv_run(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product as qgemv_run, with the same arguments and result, that allocates
+ * nothing.  Where qgemv_run would use the plan's workspace (uniform codes at
+ * batch 8/16), this call uses instead a static device array of 16 MiB that
+ * the library holds on each device it runs on until the process ends; its
+ * address is looked up once per device.  Shapes needing more (1 KiB +
+ * S * ceil(M/16) * 16 * batch * 4 bytes, S <= 8) are refused with
+ * QGEMV_ERR_SCRATCH.  Every such call on one device shares that array: calls
+ * that overlap in time (other streams, other threads, other plans) race.  The
+ * array's counters are zero at load and every completed call leaves them as
+ * it found them (a multiple of 8), so nothing needs clearing between calls.
+ * Errors: as qgemv_run (no allocation failure), plus SCRATCH.
+ */
+int qgemv_run_noalloc(qgemv_handle h, const void* x_dev, float* y_dev, int32_t batch, void* stream);
 
 /*
  * Enqueue a kernel that decodes the blob's codes back to canonical order, one

@@ -17,14 +17,14 @@ from synth import WORKLOADS, make_weights, make_x, outlier_count
 def test_library_exports_every_declared_symbol():
     L = qgemv.lib()
     names = qgemv.header_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_error_strings():
     L = qgemv.lib()
-    for st in [0, -1, -2, -3, -4, -5, 7]:
+    for st in [0, -1, -2, -3, -4, -5, -6, 7]:
         s = L.qgemv_error_string(st)
         assert isinstance(s, bytes) and len(s) > 0
     assert L.qgemv_error_string(0) == b"ok"
@@ -217,6 +217,7 @@ def test_unpack_host_rejects_inconsistent_header_fields(fmt, bits):
 def test_run_and_create_argument_checks_need_no_gpu():
     L = qgemv.lib()
     assert L.qgemv_run(None, None, None, 1, None) == -1
+    assert L.qgemv_run_noalloc(None, None, None, 1, None) == -1
     assert L.qgemv_debug_unpack(None, None, None) == -1
     assert L.qgemv_destroy(None) == 0
     h = ctypes.c_void_p(0)
