@@ -28,6 +28,10 @@ traffic, used to calibrate the HBM byte counters of a profiler run).
 --trace-summary CSV prints median / p10 / p90 of the timed replays' launches
 in a rocprofv3 kernel trace (--output-format csv) of a bench.py run given the
 same --steps and --warmup.
+--counter-summary FETCH_CSV WRITE_CSV turns two rocprofv3 counter runs
+(--pmc FETCH_SIZE, then --pmc WRITE_SIZE, each of a bench.py run with
+--copy-mb N) into the HBM bytes per launch of the path's kernel, calibrated
+on the copy kernel; --layer NAME limits a multi-layer workload to one layer.
 """
 
 from __future__ import annotations
@@ -97,16 +101,39 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, batch: int, src_hash: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_b{batch}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        t = json.load(fh)
-    if t.get("kernel_src_sha") != src_hash:
-        return None
-    return t.get("traffic_bytes_per_launch")
+def traffic_file(workload: str, batch: int, layer: str | None = None) -> str:
+    tail = f"_{layer}" if layer else ""
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_b{batch}{tail}.json")
+
+
+def load_traffic(workload: str, batch: int, src_hash: str, only_layer: str | None = None):
+    """HBM bytes per step from committed rocprofv3 counter runs, if taken on this kernel source.
+
+    A multi-layer workload has one file per distinct layer shape, named for
+    the first layer of that shape; the step's traffic is their sum over the
+    layers (None if any is missing or stale).
+    """
+    from synth import WORKLOADS
+    wl = WORKLOADS[workload]
+    if wl.layers:
+        parts = []
+        for name, M, K in wl.layers:
+            if only_layer and name != only_layer:
+                continue
+            first = next(n for n, m, k in wl.layers if (m, k) == (M, K))
+            parts.append(traffic_file(workload, batch, first))
+    else:
+        parts = [traffic_file(workload, batch)]
+    total = 0
+    for path in parts:
+        if not os.path.exists(path):
+            return None
+        with open(path) as fh:
+            t = json.load(fh)
+        if t.get("kernel_src_sha") != src_hash:
+            return None
+        total += int(t["traffic_bytes_per_launch"])
+    return total
 
 
 def csr_from_positions(M, rows, cols, values):
@@ -238,7 +265,7 @@ def time_graph(torch, launch, steps, warmup, stream, use_graph=True):
     return start.elapsed_time(end) / steps
 
 
-def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, use_graph):
+def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, use_graph, only_layer=None):
     """Per-layer timing of one workload; returns (per_layer, alg_total, ms_total, cpu_layers)."""
     import numpy as np
 
@@ -246,6 +273,8 @@ def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, u
     per_layer, cpu_layers = [], []
     alg_total, ms_total = 0, 0.0
     for layer, lname in workload_layers(workload):
+        if only_layer and lname != only_layer:
+            continue
         f = format_inputs(workload, layer)
         M, K = f["M"], f["K"]
         host_blob = qgemv.repack(f)
@@ -300,6 +329,85 @@ def read_floor(torch, qgemv, nbytes, steps, warmup, stream, dev):
     return ms * 1e3
 
 
+PATH_KERNELS = ("k_pair", "k_stream", "k_xlds", "k_split", "k_huff")
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, batch: int, layer: str | None,
+                       copy_mb: int) -> dict:
+    """HBM bytes per launch of the path's kernel from two rocprofv3 counter runs.
+
+    Each CSV holds one counter (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) for
+    every dispatch of a bench.py run with --copy-mb copy_mb.  The path's
+    kernel reads and writes the same bytes on every launch, so its value is
+    the median over its dispatches; each counter is scaled by what it reads
+    for the elementwise copy (copy_mb MiB read, copy_mb MiB written).
+    """
+    import csv
+
+    import numpy as np
+
+    def per_dispatch(path):
+        vals, names = {}, {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                d = int(r["Dispatch_Id"])
+                vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+                names[d] = r["Kernel_Name"]
+        return vals, names
+
+    out = {"workload": workload, "batch": batch}
+    if layer:
+        out["layer"] = layer
+    res = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        vals, names = per_dispatch(path)
+        ours = [v for d, v in vals.items() if any(k in names[d] for k in PATH_KERNELS)]
+        cal = [v for d, v in vals.items() if "MulFunctor" in names[d]]
+        kern = sorted({names[d].split("(")[0].replace("void ", "").replace("(anonymous namespace)::", "")
+                       for d in vals if any(k in names[d] for k in PATH_KERNELS)})
+        if not ours or not cal:
+            raise SystemExit(f"{path}: no dispatches of the path's kernels or of the calibration copy")
+        res[key] = (float(np.median(ours)), len(ours), float(np.median(cal)), kern)
+    copy_kib = copy_mb * 1024.0
+    f_kib, n, f_cal, kern = res["fetch"]
+    w_kib, _, w_cal, _ = res["write"]
+    f_scale, w_scale = copy_kib / f_cal, copy_kib / w_cal
+    traffic = f_kib * f_scale * 1024 + w_kib * w_scale * 1024
+    fi = format_inputs(workload, next(i for i, nm in workload_layers(workload) if layer in (None, nm)))
+    alg = algorithmic_bytes(fi, batch)
+    out.update({"kernels": kern, "kernel_src_sha": kernel_source_hash(),
+                "traffic_bytes_per_launch": int(round(traffic)),
+                "fetch_kib_per_dispatch": round(f_kib, 3), "write_kib_per_dispatch": round(w_kib, 3),
+                "dispatches": n, "copy_fetch_kib": f_cal, "copy_write_kib": w_cal,
+                "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+                "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4)})
+    return out
+
+
+def counter_table(path: str) -> str:
+    """Per kernel of a rocprofv3 counter run (csv): dispatches and the median of each counter per dispatch."""
+    import csv
+
+    import numpy as np
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per.setdefault(key, {})
+            per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (d, name), cs in per.items():
+        if any(k in name for k in PATH_KERNELS):
+            short = name.split("(unsigned")[0].replace("void ", "").replace("(anonymous namespace)::", "")
+            by_kernel.setdefault(short, []).append(cs)
+    counters = sorted({c for cs in per.values() for c in cs})
+    out = ["kernel | dispatches | " + " | ".join(counters)]
+    for k, lst in sorted(by_kernel.items()):
+        med = [float(np.median([cs.get(c, 0.0) for cs in lst])) for c in counters]
+        out.append(f"{k} | {len(lst)} | " + " | ".join(f"{v:.6g}" for v in med))
+    return "\n".join(out)
+
+
 def summarize_trace(path: str, steps: int, warmup: int) -> str:
     """Per-launch durations of the timed replays in a rocprofv3 kernel trace.
 
@@ -318,7 +426,7 @@ def summarize_trace(path: str, steps: int, warmup: int) -> str:
         for r in csv.DictReader(fh):
             rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
     rows.sort()
-    ours = lambda n: any(k in n for k in ("k_pair", "k_stream", "k_xlds", "k_huff"))
+    ours = lambda n: any(k in n for k in PATH_KERNELS)
     runs = []
     for t0, t1, name in rows:
         if runs and runs[-1][0] == name:
@@ -359,10 +467,23 @@ def main():
                     help="only time the read probe over windows of this many MB (rotated through 2 GiB)")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise the timed replays of a rocprofv3 kernel_trace.csv (no GPU)")
+    ap.add_argument("--layer", default=None, help="only this layer of a multi-layer workload")
+    ap.add_argument("--counter-table", default=None, metavar="CSV",
+                    help="only print per-kernel median counters of a rocprofv3 counter run (no GPU)")
+    ap.add_argument("--counter-summary", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="only turn two rocprofv3 counter runs into HBM bytes per launch (no GPU)")
     a = ap.parse_args()
 
     if a.trace_summary is not None:
         print(summarize_trace(a.trace_summary, a.steps, a.warmup))
+        return
+    if a.counter_table is not None:
+        print(counter_table(a.counter_table))
+        return
+    if a.counter_summary is not None:
+        B = a.batch or DEFAULT_BATCH.get(a.workload, 1)
+        print(json.dumps(summarize_counters(a.counter_summary[0], a.counter_summary[1], a.workload, B, a.layer,
+                                            a.copy_mb or 1024), indent=1))
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -386,12 +507,14 @@ def main():
         return
 
     per_layer, alg_total, ms_total, cpu_layers = measure(torch, qgemv, a.workload, B, a.steps, a.warmup,
-                                                         a.rotate_gib, stream, dev, not a.no_graph)
+                                                         a.rotate_gib, stream, dev, not a.no_graph, a.layer)
+    if not per_layer:
+        raise SystemExit(f"{a.workload} has no layer {a.layer!r}")
     us = ms_total * 1e3
     gbs = alg_total / (ms_total * 1e-3) / 1e9
     flops = sum(2.0 * B * p["M"] * p["K"] for p in per_layer)
     src = kernel_source_hash()
-    traffic = load_traffic(a.workload, B, src)
+    traffic = load_traffic(a.workload, B, src, a.layer)
     first = cpu_layers[0][0]
     out = {
         "metric": "µs/layer and effective GB/s (batch-1 qGEMV) as % of MI355X HBM peak",
