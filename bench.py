@@ -363,7 +363,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, batch: int
         vals, names = per_dispatch(path)
         ours = [v for d, v in vals.items() if any(k in names[d] for k in PATH_KERNELS)]
         cal = [v for d, v in vals.items() if "MulFunctor" in names[d]]
-        kern = sorted({names[d].split("(")[0].replace("void ", "").replace("(anonymous namespace)::", "")
+        kern = sorted({names[d].split("(unsigned")[0].replace("void ", "").replace("(anonymous namespace)::", "")
                        for d in vals if any(k in names[d] for k in PATH_KERNELS)})
         if not ours or not cal:
             raise SystemExit(f"{path}: no dispatches of the path's kernels or of the calibration copy")
