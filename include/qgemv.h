@@ -32,7 +32,9 @@
  * Every entry point returns an int status: QGEMV_OK (0) or a negative
  * qgemv_status.  No entry point aborts, throws or prints.  All entry points
  * are thread-safe; runs of one plan on different streams with distinct y
- * buffers may overlap.
+ * buffers may overlap, except uniform-code runs at batch 8/16, which share
+ * the plan's workspace (qgemv_run) or the device's scratch
+ * (qgemv_run_noalloc) and must not overlap in time.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
