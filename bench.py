@@ -158,6 +158,49 @@ def workload_layers(workload: str):
     return [(0, "w")]
 
 
+# Layers of a block that read the same activations: in a decoder block q, k
+# and v all take the normed hidden state, gate and up the normed attention
+# output.  With --fuse each such group runs as one product over its stacked
+# rows (one launch, x read once); the others run alone.
+FUSED_GROUPS = {"block7b_u3": (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+                               ("down", ("down",)))}
+
+
+def stack_rows(fs: list) -> dict:
+    """One weight set whose rows are the rows of fs, in order (same K, format and code width).
+
+    Every part of the storage format is per row (the code bitstream, the
+    statistics or table, the CSR rows), so stacking is concatenation; the
+    product over the stacked rows is the products of the parts, one after
+    another in y.
+    """
+    import numpy as np
+    f0 = fs[0]
+    for f in fs[1:]:
+        assert (f["K"], f["bits"], f["fmt"], f["group"]) == (f0["K"], f0["bits"], f0["fmt"], f0["group"])
+    out = {k: f0[k] for k in ("K", "bits", "fmt", "group")}
+    out["M"] = sum(f["M"] for f in fs)
+    for key in ("codes_packed", "scales", "zeros", "lut", "coefs"):
+        if key in f0:
+            out[key] = np.concatenate([f[key] for f in fs], axis=0)
+    base = np.cumsum([0] + [f["M"] for f in fs[:-1]])
+    rows = np.concatenate([np.asarray(f["rows"], np.int64) + b for f, b in zip(fs, base)])
+    cols = np.concatenate([np.asarray(f["cols"], np.int64) for f in fs])
+    vals = np.concatenate([np.asarray(f["values"], np.float16) for f in fs])
+    out["rows"], out["cols"] = rows, cols
+    out["row_ptr"], out["col_idx"], out["values"] = csr_from_positions(out["M"], rows, cols, vals)
+    return out
+
+
+def launch_units(workload: str, fuse: bool):
+    """(name, [(layer index, layer name), ...]) per launch of one step."""
+    layers = workload_layers(workload)
+    if not fuse or workload not in FUSED_GROUPS:
+        return [(name, [(i, name)]) for i, name in layers]
+    idx = {name: i for i, name in layers}
+    return [(g, [(idx[n], n) for n in members]) for g, members in FUSED_GROUPS[workload]]
+
+
 def host_description() -> dict:
     """CPU model and the BLAS build and thread count numpy runs on."""
     model = platform.machine()
@@ -265,23 +308,31 @@ def time_graph(torch, launch, steps, warmup, stream, use_graph=True):
     return start.elapsed_time(end) / steps
 
 
-def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, use_graph, only_layer=None):
-    """Per-layer timing of one workload; returns (per_layer, alg_total, ms_total, cpu_layers)."""
+def measure(torch, qgemv, workload, B, steps, warmup, rotate_gib, stream, dev, use_graph, only_layer=None,
+            fuse=False):
+    """Per-launch timing of one workload; returns (per_layer, alg_total, ms_total, cpu_layers).
+
+    Without fuse every layer is one launch; with fuse the layers of a
+    FUSED_GROUPS entry run as one launch over their stacked rows, with the
+    group's first layer's x.
+    """
     import numpy as np
 
     from synth import make_x
     per_layer, cpu_layers = [], []
     alg_total, ms_total = 0, 0.0
-    for layer, lname in workload_layers(workload):
+    for lname, members in launch_units(workload, fuse):
         if only_layer and lname != only_layer:
             continue
-        f = format_inputs(workload, layer)
+        layer = members[0][0]
+        parts = [format_inputs(workload, i) for i, _ in members]
+        f = parts[0] if len(parts) == 1 else stack_rows(parts)
         M, K = f["M"], f["K"]
         host_blob = qgemv.repack(f)
         # distinct copies whose total is >= rotate_gib; launch i reads copy i % copies
         copies = max(1, min(512, math.ceil(rotate_gib * (1 << 30) / host_blob.size)))
         plans = [qgemv.QGemv(f, device="cuda:0", blob=host_blob) for _ in range(copies)]
-        x16 = make_x(workload, B, K, layer, M)
+        x16 = make_x(workload, B, K, layer, parts[0]["M"])
         x = torch.from_numpy(x16).to(dev)
         ys = [torch.empty((B, M), dtype=torch.float32, device=dev) for _ in range(copies)]
         torch.cuda.synchronize()
@@ -467,7 +518,9 @@ def main():
                     help="only time the read probe over windows of this many MB (rotated through 2 GiB)")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise the timed replays of a rocprofv3 kernel_trace.csv (no GPU)")
-    ap.add_argument("--layer", default=None, help="only this layer of a multi-layer workload")
+    ap.add_argument("--layer", default=None, help="only this layer (or fused group) of a multi-layer workload")
+    ap.add_argument("--fuse", action="store_true",
+                    help="run the layers that share x (q,k,v; gate,up) as one product over their stacked rows")
     ap.add_argument("--counter-table", default=None, metavar="CSV",
                     help="only print per-kernel median counters of a rocprofv3 counter run (no GPU)")
     ap.add_argument("--counter-summary", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -507,14 +560,14 @@ def main():
         return
 
     per_layer, alg_total, ms_total, cpu_layers = measure(torch, qgemv, a.workload, B, a.steps, a.warmup,
-                                                         a.rotate_gib, stream, dev, not a.no_graph, a.layer)
+                                                         a.rotate_gib, stream, dev, not a.no_graph, a.layer, a.fuse)
     if not per_layer:
         raise SystemExit(f"{a.workload} has no layer {a.layer!r}")
     us = ms_total * 1e3
     gbs = alg_total / (ms_total * 1e-3) / 1e9
     flops = sum(2.0 * B * p["M"] * p["K"] for p in per_layer)
     src = kernel_source_hash()
-    traffic = load_traffic(a.workload, B, src, a.layer)
+    traffic = None if a.fuse else load_traffic(a.workload, B, src, a.layer)
     first = cpu_layers[0][0]
     out = {
         "metric": "µs/layer and effective GB/s (batch-1 qGEMV) as % of MI355X HBM peak",
@@ -532,7 +585,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": f"{a.workload}: {WORKLOAD_NOTES[a.workload]}, batch {B}", "batch": B,
+        "config": {"workload": f"{a.workload}: {WORKLOAD_NOTES[a.workload]}, batch {B}" +
+                               ("; q,k,v and gate,up each one product over their stacked rows (shared x)"
+                                if a.fuse and a.workload in FUSED_GROUPS else ""), "batch": B,
                    "bits": first.get("bits", 0), "format": first["fmt"], "layers": per_layer,
                    "timing": ("eager launches" if a.no_graph else "one HIP-graph replay of all steps per layer") +
                              ", HIP events on the launch stream; the timed replay reads weight copies the "

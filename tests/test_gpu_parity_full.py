@@ -99,3 +99,36 @@ def test_oracle_encoded_every_row(torch, name, layer, M, K, batches):
     worst = check_all(codes, runs, enc)
     say(f"[gpu]   worst |dy|/tol = {worst:.3e}")
     plan.close()
+
+
+# Layers that read the same x, run as one product over their stacked rows
+# (bench.py --fuse): each part of y is checked against its own layer's oracle.
+STACKED_CASES = [
+    ("block7b_u3", (0, 1, 2), (16, 1)),
+    ("block7b_u3", (4, 5), (16, 1)),
+]
+
+
+@pytest.mark.parametrize("name,layers,batches", STACKED_CASES)
+def test_stacked_layers_every_row(torch, name, layers, batches):
+    import bench
+    parts = [format_case(name, i) for i in layers]
+    f = bench.stack_rows(parts)
+    M, K = f["M"], f["K"]
+    say(f"[gpu] stacked bench inputs {name} layers={layers} M={M} K={K} nnz={f['row_ptr'][-1]} B={batches}")
+    plan = qgemv.QGemv(f)
+    codes = unpack_framed(torch, plan)
+    runs = []
+    for B in batches:
+        x16 = make_x(name, B, K, layers[0], parts[0]["M"])
+        y = run_framed(torch, plan, x16)
+        assert np.array_equal(y, run_framed(torch, plan, x16)), f"B={B}: not bitwise deterministic"
+        runs.append((y, x16))
+    worst, r0 = 0.0, 0
+    for p in parts:
+        rows = slice(r0, r0 + p["M"])
+        w = check_all(codes[rows], [(y[:, rows], x16) for y, x16 in runs], p)
+        worst = max(worst, w)
+        r0 += p["M"]
+    say(f"[gpu]   worst |dy|/tol = {worst:.3e}")
+    plan.close()
