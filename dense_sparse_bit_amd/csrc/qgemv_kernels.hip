@@ -1147,7 +1147,7 @@ k_split(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ meta, co
   const rsrc_t rbe = make_rsrc(bent, (uint32_t)nnz * 4);
 
   // Prologue: the block outlier offsets and the tables, then the x slice
-  // straight into LDS; all of it lands before the code ring is issued.
+  // straight into LDS, then the first chunk's code loads (below).
   int bo[2] = {0, 0};  // offsets of (local tile, block) pairs tid and tid + 1024
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
