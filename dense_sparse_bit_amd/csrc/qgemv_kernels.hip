@@ -2185,9 +2185,10 @@ size_t split_lds(const BlobHeader& h, int nb, int S, int NG, int CH) {
 }
 
 // The first (S, CH) in order of preference that fits: S = 4 keeps a quarter
-// of x per CU with one read-back per group of four; S = 8 for long K; larger
-// chunks when the chunk partials would not fit.  The staged offsets of a
-// workgroup must fit two per thread.
+// of x per CU with one read-back per group of four; S = 8 for long K.
+// Single-block chunks where their partials fit (more chunks per wave, so the
+// older waves of a SIMD take more of them), larger chunks otherwise.  The
+// staged offsets of a workgroup must fit two per thread.
 bool split_config(const BlobHeader& h, int nb, SplitCfg& c) {
   // Uniform codes only: LUT and BPDQ decodes are bound by the VALU, not by x.
   if (h.format != QGEMV_FMT_UNIFORM) return false;
@@ -2197,7 +2198,7 @@ bool split_config(const BlobHeader& h, int nb, SplitCfg& c) {
     if (NG >= 8) NG &= ~7;
     const int tw = (h.tiles + NG - 1) / NG, kbm = (h.nkb + S - 1) / S;
     if (tw * ((kbm + 4) & ~3) > 2 * 64 * kWaves) continue;
-    for (int CH : {2, 4, 8}) {
+    for (int CH : {1, 2, 4, 8}) {
       const size_t lds = split_lds(h, nb, S, NG, CH);
       if (lds > kLdsBytes) continue;
       c.S = S;
@@ -2237,6 +2238,7 @@ hipError_t launch_split_ch(const qgemv_plan* p, const SplitCfg& c, const uint16_
 template <int FMT, int BITS, int NB>
 hipError_t launch_split(const qgemv_plan* p, const SplitCfg& c, const uint16_t* x, float* y, void* ws,
                         hipStream_t st) {
+  if (c.CH == 1) return launch_split_ch<FMT, BITS, NB, 1>(p, c, x, y, ws, st);
   return c.CH == 2   ? launch_split_ch<FMT, BITS, NB, 2>(p, c, x, y, ws, st)
          : c.CH == 4 ? launch_split_ch<FMT, BITS, NB, 4>(p, c, x, y, ws, st)
                      : launch_split_ch<FMT, BITS, NB, 8>(p, c, x, y, ws, st);
