@@ -2040,9 +2040,8 @@ bool stream_xst(const BlobHeader& h, int nb, int ch) {
   return g == stream_grid(h, nb, ch, false) && stream_lds_fixed(h, g, nb, ch, true) <= kLdsBytes;
 }
 
-template <int FMT, int BITS, int NB, bool XST>
+template <int FMT, int BITS, int NB, bool XST, int CH>
 hipError_t launch_stream_x(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int CH = NB == 1 ? 2 : 3;  // K-blocks per chunk
   constexpr int NR = 1;                // chunks in flight per wave
   const BlobHeader& h = p->h;
   const int grid = stream_grid(h, NB, CH, XST);
@@ -2075,10 +2074,17 @@ hipError_t launch_stream_x(const qgemv_plan* p, const uint16_t* x, float* y, hip
 template <int FMT, int BITS, int NB>
 hipError_t launch_stream(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
   if constexpr (NB == 1) {
-    return launch_stream_x<FMT, BITS, NB, false>(p, x, y, st);
+    // K-blocks per chunk at batch 1: single blocks when a workgroup holds one
+    // tile (its 16 waves then share the tile's blocks more finely) and for
+    // BPDQ codes, whose decode keeps a wave longest per block; pairs
+    // otherwise.
+    const bool one = FMT == QGEMV_FMT_BPDQ || (p->h.tiles + stream_grid(p->h, 1, 2, false) - 1) /
+                                                      stream_grid(p->h, 1, 2, false) <= 1;
+    return one ? launch_stream_x<FMT, BITS, NB, false, 1>(p, x, y, st)
+               : launch_stream_x<FMT, BITS, NB, false, 2>(p, x, y, st);
   } else {
-    return stream_xst(p->h, NB, 3) ? launch_stream_x<FMT, BITS, NB, true>(p, x, y, st)
-                                   : launch_stream_x<FMT, BITS, NB, false>(p, x, y, st);
+    return stream_xst(p->h, NB, 3) ? launch_stream_x<FMT, BITS, NB, true, 3>(p, x, y, st)
+                                   : launch_stream_x<FMT, BITS, NB, false, 3>(p, x, y, st);
   }
 }
 
