@@ -2114,7 +2114,8 @@ bool xlds_fits(const BlobHeader& h, int nb) {
 
 template <int FMT, int BITS, int NB>
 hipError_t launch_xlds(const qgemv_plan* p, const uint16_t* x, float* y, hipStream_t st) {
-  constexpr int R = 4;  // code ring slots per wave
+  // code ring slots per wave: 4 for 4-bit codes (1 KiB per block), 3 for 3-bit
+  constexpr int R = BITS == 4 ? 4 : 3;
   const BlobHeader& h = p->h;
   const int grid = xlds_grid(h);
   const size_t fixed = xlds_fixed(h, grid, NB);
