@@ -566,6 +566,88 @@ def test_lloyd_recovers_exact_clusters():
     assert np.array_equal(gemv.decode(enc), W.astype(np.float64))
 
 
+def check_weighted_quantile(wq):
+    """Lower inverse CDF of the weighted sample, at hand-computed levels.
+
+    w = (3, 1, 2, 5) with weights (1, 1, 2, 0): sorted 1, 2, 3, 5 with
+    cumulative fractions 0.25, 0.75, 1, 1.
+    """
+    w = np.array([3.0, 1.0, 2.0, 5.0])
+    s = np.array([1.0, 1.0, 2.0, 0.0])
+    got = wq(w, s, [0.1, 0.25, 0.26, 0.75, 0.9, 1.0])
+    if got.tolist() != [1.0, 1.0, 2.0, 2.0, 3.0, 3.0]:
+        return False
+    # equal weights: the level 1/2 of 1..5 is the lower median
+    return wq(np.arange(1.0, 6.0), np.ones(5), [0.5]).tolist() == [3.0]
+
+
+def test_weighted_quantile_pin():
+    assert check_weighted_quantile(encode.weighted_quantile)
+
+
+def test_weighted_quantile_catches_upper_inverse():
+    def upper(w, s, qs):
+        order = np.argsort(w, kind="stable")
+        cw = np.cumsum(s[order]) / s.sum()
+        idx = np.searchsorted(cw, np.asarray(qs, dtype=np.float64), side="right")
+        return w[order][np.minimum(idx, len(w) - 1)]
+    assert not check_weighted_quantile(upper)
+
+
+def test_weighted_quantile_catches_dropped_weights():
+    assert not check_weighted_quantile(lambda w, s, qs: encode.weighted_quantile(w, np.ones_like(s), qs))
+
+
+def check_lloyd_first_steps(lloyd):
+    """Initialisation at the weighted levels (k + 1/2)/(C - 1) and one
+    assign-and-update step, by hand, on w = 1..12.
+
+    Equal weights, C = 4: the levels 1/6, 1/2, 5/6 give the free centroids
+    2, 6, 10 next to the pinned 0.  One step: 1 ties between 0 and 2 and goes
+    to 0 (the lower), 2, 3, 4 (tie) go to 2, 5..8 (8 ties) to 6, 9..12 to 10;
+    the new centroids are the means 3, 6.5 and 10.5.  With weight 3 on w = 4
+    the first free centroid moves to (2 + 3 + 12) / 5 = 3.4 instead, and with
+    weight 11 on w = 12 (and 1 elsewhere) the initial free centroids are 4,
+    11 and 12.
+    """
+    w = np.arange(1.0, 13.0)
+    ones = np.ones(12)
+    init, _ = lloyd(w, ones, 4, max_iter=0)
+    one, _ = lloyd(w, ones, 4, max_iter=1)
+    s4 = ones.copy()
+    s4[3] = 3.0
+    one4, _ = lloyd(w, s4, 4, max_iter=1)
+    s12 = ones.copy()
+    s12[11] = 11.0
+    init12, _ = lloyd(w, s12, 4, max_iter=0)
+    return (init.tolist() == [0.0, 2.0, 6.0, 10.0] and one.tolist() == [0.0, 3.0, 6.5, 10.5]
+            and abs(one4[1] - 3.4) < 1e-12 and init12.tolist() == [0.0, 4.0, 11.0, 12.0])
+
+
+def test_lloyd_first_steps_pin():
+    assert check_lloyd_first_steps(encode.lloyd_row)
+
+
+def test_lloyd_first_steps_catch_levels_without_the_half(monkeypatch):
+    orig = encode.weighted_quantile
+    monkeypatch.setattr(encode, "weighted_quantile",
+                        lambda w, s, qs: orig(w, s, np.asarray(qs) - 0.5 / (len(qs))))
+    assert not check_lloyd_first_steps(encode.lloyd_row)
+
+
+def test_lloyd_first_steps_catch_unweighted_update():
+    def unweighted(w, s, C, max_iter=100, history=None):
+        # the oracle's own steps with the mean update dropping the weights
+        cent, zi = encode.lloyd_row(w, s, C, max_iter=0)
+        for _ in range(max_iter):
+            a = encode.nearest(w, cent)
+            for c in range(C):
+                if c != zi and np.any(a == c):
+                    cent[c] = w[a == c].mean()
+        return cent, zi
+    assert not check_lloyd_first_steps(unweighted)
+
+
 def test_lut_codes_nearest_and_zero_pinned():
     wl, W, planted, x, enc = small("mlp7b_lut3")
     lut = enc["lut"].astype(np.float64)
